@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged key/value cache on one MI355X.
+
+Workload (default): GQA decode, 32 layers run in sequence, 32 query / 8
+key-value heads, head dim 128, bf16, batch 64 with context lengths uniform in
+[512, 4096], block size 16, pool of 1.25x the used blocks with shuffled
+physical blocks.  A step is the whole path for one new token per sequence:
+host block manager (slots, copy-on-write pairs), upload of tables, block
+copies, then for every layer the cache write of the new token and the paged
+decode attention.  Inputs are seeded synthetic values resident in device
+memory before timing starts.
+
+Prints one JSON line: whole-step throughput in algorithmic GB/s (cache bytes
+the method must move: the useful key/value positions, queries, outputs,
+tables, and the written and copied bytes), seq-steps/s, the roofline of the
+attention kernel (HIP events around every launch in the timed region), and
+the fp64 CPU oracle timed on a bounded sample of the same step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_239_amd", "csrc", "pa_device.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_attention_gqa32x8_bf16_b16_pmc.md")
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None if that summary was taken on another
+    version of the kernel source."""
+    try:
+        text = open(PMC_SUMMARY).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return rec
+
+
+def attn_bytes(lens, S, Hq, Hkv, d, B, b=2) -> int:
+    """Algorithmic bytes of one layer's decode attention."""
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(np.sum(lens)) * 2 * Hkv * d * b
+    qo = 2 * S * Hq * d * b
+    meta = int(np.sum((lens + B - 1) // B)) * 4 + S * 4
+    return kv + qo + meta
+
+
+def write_bytes(S, Hkv, d, b=2) -> int:
+    return 2 * (2 * S * Hkv * d * b) + 8 * S
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (3 = the GQA 32/8 workload)")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference for "
+                         "hardware byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
+                                   "part of this build (each GPU would hold its own shard of heads "
+                                   "or sequences with no exchange inside attention)",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    from paged_kv_cache_239_amd.engine import DecodeEngine
+    from workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    torch.cuda.set_device(0)
+    if args.calibrate:
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": src.numel() * 4, "copies": 3}))
+        return 0
+
+    wl = make_workload(args.config)
+    c = wl.cfg
+    W, K = args.warmup, args.steps
+    eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(W + K),
+                       free_order=wl.free_order)
+    # seeded N(0,1) pool contents (device RNG), then the prefill history on the native manager
+    for layer in range(c.L):
+        for which in ("k", "v"):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(wl.pool_fill_seed(layer, which))
+            eng.pool.slab(layer, which).normal_(generator=g)
+    for op in wl.history:
+        if op[0] == "append":
+            eng.append(op[1], op[2])
+        else:
+            eng.fork(op[1], op[2], op[3])
+    eng.upload_tables()
+
+    def dev(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.bfloat16 if c.dtype == "bf16" else torch.float16).cuda()
+
+    # per-layer inputs of the step (the same values every step)
+    qs = {l: dev(wl.q_bits(l, 0)) for l in range(c.L)}
+    ks = {l: dev(wl.knew_bits(l, 0)) for l in range(c.L)}
+    vs = {l: dev(wl.vnew_bits(l, 0)) for l in range(c.L)}
+    outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+    scale = float(wl.scale)
+
+    snap_layers = sorted(set([0, c.L // 2, c.L - 1] + list(range(0, c.L, max(1, c.L // 8)))))
+    snaps = {}
+    if args.cpu_baseline == "on":
+        for layer in snap_layers:
+            snaps[layer] = tuple(eng.pool.slab(layer, w).view(torch.int16).cpu().numpy().view(np.uint16)
+                                 for w in ("k", "v"))
+    torch.cuda.synchronize()
+
+    for _ in range(W):
+        max_ctx = eng.manager_step()
+        eng.device_step(qs, ks, vs, outs, max_ctx, scale)
+    torch.cuda.synchronize()
+
+    step_events, attn_events = [], []
+    alg_bytes = 0
+    attn_alg = []
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    issue_ms = []
+    for _ in range(K):
+        es = torch.cuda.Event(enable_timing=True)
+        ee = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        es.record()
+        max_ctx = eng.manager_step()
+        eng.device_step(qs, ks, vs, outs, max_ctx, scale, attn_events=attn_events)
+        ee.record()
+        issue_ms.append((time.perf_counter() - h0) * 1e3)
+        step_events.append((es, ee))
+        ab = attn_bytes(eng.lens, wl.S, c.Hq, c.Hkv, c.d, c.B)
+        attn_alg.extend([ab] * c.L)
+        alg_bytes += c.L * (ab + write_bytes(wl.S, c.Hkv, c.d))
+        alg_bytes += len(eng.last_pairs) * c.L * 2 * eng.pool.nbytes // (2 * c.L * wl.P) * 2
+    ev1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / K
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_events])
+    attn_ms = np.array([a.elapsed_time(b) for a, b in attn_events])
+    mean_attn_bytes = float(np.mean(attn_alg))
+    attn_avg_us = float(np.mean(attn_ms)) * 1e3
+    achieved = mean_attn_bytes / (attn_avg_us * 1e-6) / 1e9
+    value = alg_bytes / (total_ms * 1e-3) / 1e9
+    seq_steps = wl.S * K / (total_ms * 1e-3)
+
+    result = {
+        "metric": "paged decode-attn achieved HBM GB/s (% of MI355X peak) + seq-steps/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.name}: GQA decode, {c.L} layers in sequence, {c.Hq} query / {c.Hkv} KV heads, "
+                        f"d={c.d}, {c.dtype}, batch {wl.S}, context uniform in [512,4096] (+1 per step), "
+                        f"block {c.B}, pool {wl.P} blocks (1.25x used, shuffled)",
+            "global_batch": wl.S,
+            "layers": c.L,
+            "block_size": c.B,
+            "pool_gib": round(eng.pool.nbytes / 2 ** 30, 2),
+            "parallelism": "single GPU",
+        },
+        "seq_steps_per_s": round(seq_steps, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "wall_ms_per_step": round((wall1 - wall0) * 1e3 / K, 4),
+        "attn_launch_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "roofline": {
+            "kernel": "decode_attention_kernel<bf16,G=4,B=16>",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "traffic_note": "no counter summary for this kernel source",
+            "alg_bytes_per_launch": int(mean_attn_bytes),
+            "avg_launch_us": round(attn_avg_us, 2),
+        },
+    }
+
+    rec = recorded_traffic()
+    if rec is not None:
+        result["roofline"]["traffic"] = int(rec["traffic_bytes_per_launch"])
+        result["roofline"]["traffic_note"] = (
+            f"rocprofv3 FETCH_SIZE x{rec['fetch_scale']} + WRITE_SIZE x{rec['write_scale']} per launch "
+            f"(scales from a plain copy of known size), at {rec['alg_bytes_per_launch']} algorithmic bytes; "
+            f"traffic / algorithmic = {rec['traffic_over_alg']}")
+    result["host_issue_ms_per_step_p50"] = round(float(np.median(issue_ms)), 4)
+    if args.dump:
+        with open(args.dump, "w") as f:
+            json.dump({"step_ms": step_ms.tolist(), "attn_us": (attn_ms * 1e3).tolist(), "issue_ms": issue_ms}, f)
+    if args.cpu_baseline == "on":
+        result["cpu_baseline"], result["parity"] = cpu_baseline(wl, eng, snaps, outs, W + K, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, eng, snaps, outs, total_steps, budget_s):
+    """The fp64 oracle on a bounded sample of the final timed step: its own
+    manager replays the history and every step, its own host pools (from the
+    pre-step snapshots) receive every step's writes, then whole layers of the
+    final step are recomputed until the time budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle.cache_ops import HostPool, copy_blocks, write_kv
+    from oracle.decode import decode_one
+    from oracle.dtypes import bits_to_f64
+    from oracle.replay import build_state, manager_step
+
+    c = wl.cfg
+    st = build_state(wl, maxb=eng.maxb)
+    pools = {l: HostPool.from_arrays(k[None], v[None]) for l, (k, v) in snaps.items()}
+    for _ in range(total_steps):
+        slots, pairs, lens = manager_step(st)
+        for l, pool in pools.items():
+            copy_blocks(pool, pairs)
+            write_kv(pool, 0, wl.knew_bits(l, 0), wl.vnew_bits(l, 0), slots)
+    tables_match = bool(np.array_equal(np.asarray(st.lens), eng.lens)) and all(
+        list(eng.tables[s, : -(-st.lens[s] // c.B)]) == st.tables[s][: -(-st.lens[s] // c.B)]
+        for s in range(wl.S))
+
+    import torch
+    done, nbytes, worst_abs, worst_rel, worst_all = 0, 0, 0.0, 0.0, 0.0
+    layers_done = []
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for l in snaps:
+            q = wl.q_bits(l, 0)
+            got = bits_to_f64(outs[l].view(torch.int16).cpu().numpy().view(np.uint16), c.dtype)
+            for s in range(wl.S):
+                ref = decode_one(pools[l], 0, q[s], st.tables[s], st.lens[s], float(wl.scale), c.dtype)
+                err = np.abs(got[s] - ref)
+                big = np.abs(ref) >= 0.2
+                worst_all = max(worst_all, float(err.max()))
+                if np.any(~big):
+                    worst_abs = max(worst_abs, float(err[~big].max()))
+                if np.any(big):
+                    worst_rel = max(worst_rel, float(np.max(err[big] / np.abs(ref[big]))))
+                nbytes += attn_bytes([st.lens[s]], 1, c.Hq, c.Hkv, c.d, c.B)
+                done += 1
+            layers_done.append(l)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        t1 = time.perf_counter()
+    secs = t1 - t0
+    baseline = {
+        "value": round(nbytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "seq_steps_per_s": round(done / c.L / secs, 3),
+        "seconds": round(secs, 2),
+        "sample": f"final timed step, layers {layers_done} x all {wl.S} sequences "
+                  f"({done} sequence-layers of {wl.S * c.L}); numpy fp64 gather + dense attention, "
+                  f"BLAS limited to 1 thread; seq-steps/s scaled by 1/{c.L} layers",
+    }
+    parity = {"sampled_seq_layers": done, "max_abs": worst_all, "max_abs_where_ref_below_0.2": worst_abs,
+              "max_rel_where_ref_at_least_0.2": worst_rel,
+              "tolerance": {"max_abs": 2e-3, "max_rel": 1e-2},
+              "pass": bool(worst_abs <= 2e-3 and worst_rel <= 1e-2 and tables_match),
+              "tables_bit_exact": tables_match}
+    return baseline, parity
+
+
+if __name__ == "__main__":
+    sys.exit(main())

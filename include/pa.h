@@ -1,0 +1,253 @@
+/*
+ * pa.h -- C ABI of the paged key/value cache and decode-attention library
+ * for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources, by page title and section):
+ *
+ *  - "vLLM PagedAttention and continuous batching" (netleverage.com),
+ *    section "PagedAttention: fixed blocks, non-contiguous physical memory":
+ *    a sequence's keys and values live in fixed-size blocks of B token slots;
+ *    a per-sequence block table maps logical block j to a physical block; a
+ *    block engine slices one contiguous device allocation into physical
+ *    blocks; a new physical block is taken only when the previous one is full.
+ *  - same article, section "Sharing with reference counts and
+ *    copy-on-write": each physical block carries a reference count; a write
+ *    into a block with count > 1 takes a new block, copies that block and
+ *    drops the old count; a block at count 0 is released; the policies are
+ *    fork, append and free; the kernel sees only physical block ids.
+ *  - same article, section "The kernel page, and what the 2023 runs
+ *    measured": a single-query decode kernel with separate key and value
+ *    caches and a compile-time block size.
+ *  - "Serving Language Models Within a Memory Budget" (auturnal.com),
+ *    section 6 and eq. (4): dense scaled-dot-product attention evaluated
+ *    block by block with a running maximum and normaliser; the same rescale
+ *    merges partial results.
+ *  - "PagedAttention and Online Inference" (auturnal.com), section 1:
+ *    grouped-query attention has fewer key/value heads than query heads.
+ *    Query head h reads key/value head floor(h / G), G = Hq / Hkv.
+ *
+ * Conventions for every call:
+ *  - Return value: PA_OK (0) or a negative pa_status.  No call aborts or
+ *    throws across the ABI.  After a failure, pa_last_error() returns a
+ *    message for the calling thread (valid until that thread's next call).
+ *  - "host" pointers are CPU memory; "device" pointers are GPU memory on
+ *    the device that is current for the calling thread.  The caller owns
+ *    every buffer it passes; the library never frees caller memory.
+ *  - Device operations are asynchronous on the given HIP stream (0 = the
+ *    null stream) and return after enqueueing.  Launch failures return
+ *    PA_ERR_HIP with the HIP error string in pa_last_error().
+ *  - The host block manager is synchronous and not thread-safe: serialise
+ *    calls that use the same pool.
+ *  - Storage type: Q, K, V and the attention output share one 16-bit type
+ *    (pa_dtype).  Arithmetic is fp32; the output is rounded to nearest even.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as the HIP runtime's own; repeating it is legal. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* a null pointer, bad size, bad id, misalignment */
+  PA_ERR_OUT_OF_BLOCKS = -2, /* the free list is empty; manager state unchanged */
+  PA_ERR_UNSUPPORTED = -3,   /* a shape with no compiled kernel (see below)   */
+  PA_ERR_HIP = -4            /* a HIP runtime call or launch failed            */
+} pa_status;
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef struct pa_pool pa_pool; /* opaque, host-owned */
+
+typedef struct {
+  int64_t allocs;          /* blocks taken from the free list            */
+  int64_t cows;            /* copy-on-write block copies requested       */
+  int64_t releases;        /* blocks returned to the free list           */
+  int32_t live_blocks;     /* blocks with refcount > 0 now               */
+  int32_t live_high_water; /* largest live_blocks seen                   */
+  int32_t free_blocks;     /* blocks on the free list now                */
+  int32_t num_blocks;      /* P                                          */
+} pa_pool_stats;
+
+/* ---------------------------------------------------------------------
+ * Pool ("block engine")
+ * ------------------------------------------------------------------- */
+
+/* Bytes of device memory a pool of P blocks needs:
+ *   L * 2 * P * Hkv * B * d * 2
+ * (key/value cache bytes of eq. (1) of the memory-budget page with P*B
+ * retained slots).  Returns 0 if any argument is not positive or the
+ * product overflows. */
+size_t pa_pool_bytes(int L, int Hkv, int d, int B, int P, pa_dtype dtype);
+
+/* Create a pool over caller-provided device memory.
+ *   dev_base  : device, 256-byte aligned, at least pa_pool_bytes(...) bytes.
+ *               Layout, layer-major with separate key and value slabs:
+ *                 K of layer l at dev_base + (2l)   * slab
+ *                 V of layer l at dev_base + (2l+1) * slab
+ *                 slab = P * Hkv * B * d * 2 bytes, each slab [P][Hkv][B][d].
+ *   free_order: host [P], a permutation of 0..P-1 that seeds the FIFO free
+ *               list (allocation takes the head, release appends at the
+ *               tail), or NULL for 0..P-1.
+ * The pool does not touch dev_base (no kernel runs here) and never frees it.
+ * Errors: INVALID_ARG for non-positive sizes, a size product that
+ * overflows, misaligned or short memory, or a free_order that is not a
+ * permutation. */
+pa_status pa_alloc_pool(pa_pool** out, int L, int Hkv, int d, int B, int P,
+                        pa_dtype dtype, void* dev_base, size_t dev_bytes,
+                        const int32_t* free_order);
+void pa_free_pool(pa_pool* pool); /* host metadata only; NULL is a no-op */
+
+/* Device addresses of layer `layer`'s key and value slabs. */
+pa_status pa_pool_layer_ptrs(const pa_pool* pool, int layer, void** k_slab,
+                             void** v_slab);
+
+/* ---------------------------------------------------------------------
+ * Host block manager (bit-exact, synchronous, not thread-safe)
+ * Block tables are host int32 arrays of `maxb` entries; entry j is the
+ * physical block of logical block j (tokens jB..jB+B-1).  A sequence of n
+ * tokens uses entries 0..ceil(n/B)-1; the rest are ignored.
+ * ------------------------------------------------------------------- */
+
+/* Pop the head of the free list; the block gets refcount 1. */
+pa_status pa_block_alloc(pa_pool* pool, int32_t* blk);
+/* One more reference to a live block (INVALID_ARG if free or out of range). */
+pa_status pa_block_incref(pa_pool* pool, int32_t blk);
+/* Drop one reference; at 0 the block goes to the tail of the free list.
+ * INVALID_ARG for a block that is already free (double free). */
+pa_status pa_block_decref(pa_pool* pool, int32_t blk);
+/* Current refcount, or -1 if blk is out of range. */
+int32_t pa_block_refcount(const pa_pool* pool, int32_t blk);
+int32_t pa_num_free_blocks(const pa_pool* pool);
+/* Copy the free list, head first, into host out[cap]; *count = its length. */
+pa_status pa_free_list(const pa_pool* pool, int32_t* out, int32_t cap,
+                       int32_t* count);
+pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
+
+/* Append one token to a sequence holding n_before tokens (its new token
+ * goes to position n_before):
+ *   - n_before % B == 0: take a new block for logical block n_before / B;
+ *   - else if the block holding position n_before has refcount > 1
+ *     (copy-on-write): take a new block, report (*cow_src, *cow_dst) =
+ *     (old, new), drop one reference to old, point the table at new;
+ *   - slot = phys * B + n_before % B.
+ * The caller must copy cow_src to cow_dst (pa_copy_blocks) before writing
+ * the token (pa_write_kv).  *cow_src = *cow_dst = -1 when no copy is needed.
+ * On OUT_OF_BLOCKS nothing changes.  INVALID_ARG if n_before / B >= maxb or
+ * the table maps a free block. */
+pa_status pa_append_slot(pa_pool* pool, int32_t* table, int32_t maxb,
+                         int32_t n_before, int64_t* slot, int32_t* cow_src,
+                         int32_t* cow_dst);
+
+/* `count` successive appends to one sequence (prefill).  slots: host
+ * [count] or NULL; cow_pairs: host [count][2] or NULL; *n_pairs = copies
+ * requested; *n_done = appends completed.  On failure the first *n_done
+ * appends stay applied and the failing one changed nothing. */
+pa_status pa_append_tokens(pa_pool* pool, int32_t* table, int32_t maxb,
+                           int32_t n_before, int32_t count, int64_t* slots,
+                           int32_t* cow_pairs, int32_t* n_pairs,
+                           int32_t* n_done);
+
+/* One decode step for S sequences, processed in batch order (the first
+ * writer into a shared block copies; the one that finds refcount 1 writes
+ * in place).  tables: host [S][maxb] (edited in place); n_before: host [S];
+ * slots: host [S]; cow_pairs: host [S][2]; *n_pairs, *n_done as above. */
+pa_status pa_append_batch(pa_pool* pool, int32_t* tables, int32_t maxb,
+                          const int32_t* n_before, int32_t S, int64_t* slots,
+                          int32_t* cow_pairs, int32_t* n_pairs,
+                          int32_t* n_done);
+
+/* Fork: child_table[0..nb-1] = parent_table[0..nb-1] and one more reference
+ * to each of those blocks, nb = ceil(n_tokens / B).  Nothing changes on
+ * error. */
+pa_status pa_seq_fork(pa_pool* pool, const int32_t* parent_table,
+                      int32_t n_tokens, int32_t* child_table, int32_t maxb);
+
+/* Free: one reference fewer for each of the sequence's ceil(n_tokens/B)
+ * blocks.  INVALID_ARG (and nothing changes) if a block would drop below
+ * zero. */
+pa_status pa_seq_free(pa_pool* pool, const int32_t* table, int32_t n_tokens);
+
+/* ---------------------------------------------------------------------
+ * Device operations ("fused block operations" of the reading guide
+ * "Efficient Memory Management for Large Language Model Serving with
+ * PagedAttention", section "Main concepts to understand")
+ * ------------------------------------------------------------------- */
+
+/* reshape_and_cache: token s's key and value, k[s] and v[s] (device,
+ * [S][Hkv][d], 16-byte aligned, pool dtype), go to slot slot_mapping[s]
+ * (device int64 [S]) of layer `layer`: block slot / B, offset slot % B, for
+ * every key/value head.  A negative slot skips the token; a slot >= P*B is
+ * ignored as well (never written).  Bitwise copy, no type change.
+ * Slots of one call must be distinct. */
+pa_status pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
+                      const int64_t* slot_mapping, int S, hipStream_t stream);
+
+/* copy_blocks: for each pair (src, dst) in pairs (device int32 [N][2]) copy
+ * the whole physical block -- every layer, keys and values, all B slots and
+ * Hkv heads -- from src to dst.  Pairs with an id outside [0, P) or src ==
+ * dst are skipped.  Destinations must be distinct and must not appear as a
+ * source in the same call. */
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N,
+                         hipStream_t stream);
+
+/* Workspace for pa_decode_attention calls with up to S sequences, Hq query
+ * heads and max_ctx context: split-K partial results (fp32 running maximum,
+ * normaliser and weighted value sum per query head and context partition).
+ * The size never decreases with S or max_ctx, so one workspace sized for the
+ * largest call serves every smaller one.  Returns 0 for max_ctx == 0 or
+ * invalid arguments. */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int S, int Hq,
+                                 int max_ctx);
+
+/* Zero a workspace.  Optional: every partial a call reads was written by the
+ * same call. */
+pa_status pa_decode_workspace_init(void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Decode-step paged attention for layer `layer`: for each sequence s and
+ * query head h,
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) V[t]
+ * over context positions t = 0..context_lens[s]-1, where K[t], V[t] are key
+ * and value head floor(h / (Hq/Hkv)) of slot t % B of physical block
+ * block_tables[s][t / B].
+ *   out, q        : device [S][Hq][d], pool dtype, 16-byte aligned.
+ *   block_tables  : device int32 [S][maxb].
+ *   context_lens  : device int32 [S], each in [0, max_ctx]; 0 gives zeros.
+ *   max_ctx       : host; an upper bound of context_lens (sizes the grid);
+ *                   must be <= maxb * B.
+ *   workspace     : device, 256-byte aligned, >= pa_decode_workspace_bytes(
+ *                   pool, S, Hq, max_ctx) bytes; may be NULL when that size
+ *                   is 0.  Calls that overlap in time need separate
+ *                   workspaces.
+ * Supported: d = 128, B in {16, 32}, Hq / Hkv in {1, 2, 4, 8}; other shapes
+ * return UNSUPPORTED.  Device-side values are trusted for results but
+ * clamped for memory safety: a table entry outside [0, P) reads block
+ * min(max(entry, 0), P-1) and a length above max_ctx is cut to max_ctx.
+ * Context positions are read only through entries 0..ceil(len/B)-1 of a
+ * table; slots past a sequence's length never influence its output. */
+pa_status pa_decode_attention(pa_pool* pool, int layer, void* out,
+                              const void* q, int S, int Hq,
+                              const int32_t* block_tables, int maxb,
+                              const int32_t* context_lens, int max_ctx,
+                              float scale, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Message describing the calling thread's last failure ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* PA_H */

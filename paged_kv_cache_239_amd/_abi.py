@@ -1,0 +1,127 @@
+"""ctypes declarations of the C ABI in include/pa.h.
+
+Argument marshalling only: every computation happens in the native library.
+Loading fails loudly if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+HOST_LIB_PATH = os.path.join(HERE, "libpa_host.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_OUT_OF_BLOCKS = -2
+PA_ERR_UNSUPPORTED = -3
+PA_ERR_HIP = -4
+
+PA_F16 = 0
+PA_BF16 = 1
+
+_STATUS_NAMES = {
+    PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG",
+    PA_ERR_OUT_OF_BLOCKS: "PA_ERR_OUT_OF_BLOCKS",
+    PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
+    PA_ERR_HIP: "PA_ERR_HIP",
+}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str, n_done: int = 0):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.n_done = n_done
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+class pa_pool_stats(C.Structure):
+    _fields_ = [
+        ("allocs", C.c_int64),
+        ("cows", C.c_int64),
+        ("releases", C.c_int64),
+        ("live_blocks", C.c_int32),
+        ("live_high_water", C.c_int32),
+        ("free_blocks", C.c_int32),
+        ("num_blocks", C.c_int32),
+    ]
+
+
+P = C.c_void_p
+I32 = C.c_int32
+I64 = C.c_int64
+PI32 = C.POINTER(C.c_int32)
+PI64 = C.POINTER(C.c_int64)
+
+# name -> (restype, argtypes); device entry points are absent from the
+# host-only build.
+HOST_SIGNATURES = {
+    "pa_pool_bytes": (C.c_size_t, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int]),
+    "pa_alloc_pool": (C.c_int, [C.POINTER(P), C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                P, C.c_size_t, PI32]),
+    "pa_free_pool": (None, [P]),
+    "pa_pool_layer_ptrs": (C.c_int, [P, C.c_int, C.POINTER(P), C.POINTER(P)]),
+    "pa_block_alloc": (C.c_int, [P, PI32]),
+    "pa_block_incref": (C.c_int, [P, I32]),
+    "pa_block_decref": (C.c_int, [P, I32]),
+    "pa_block_refcount": (I32, [P, I32]),
+    "pa_num_free_blocks": (I32, [P]),
+    "pa_free_list": (C.c_int, [P, PI32, I32, PI32]),
+    "pa_pool_get_stats": (C.c_int, [P, C.POINTER(pa_pool_stats)]),
+    "pa_append_slot": (C.c_int, [P, PI32, I32, I32, PI64, PI32, PI32]),
+    "pa_append_tokens": (C.c_int, [P, PI32, I32, I32, I32, PI64, PI32, PI32, PI32]),
+    "pa_append_batch": (C.c_int, [P, PI32, I32, PI32, I32, PI64, PI32, PI32, PI32]),
+    "pa_seq_fork": (C.c_int, [P, PI32, I32, PI32, I32]),
+    "pa_seq_free": (C.c_int, [P, PI32, I32]),
+    "pa_last_error": (C.c_char_p, []),
+    "pa_version": (C.c_char_p, []),
+}
+
+DEVICE_SIGNATURES = {
+    "pa_write_kv": (C.c_int, [P, C.c_int, P, P, P, C.c_int, P]),
+    "pa_copy_blocks": (C.c_int, [P, P, C.c_int, P]),
+    "pa_decode_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int]),
+    "pa_decode_workspace_init": (C.c_int, [P, C.c_size_t, P]),
+    "pa_decode_attention": (C.c_int, [P, C.c_int, P, P, C.c_int, C.c_int, P, C.c_int, P, C.c_int,
+                                      C.c_float, P, C.c_size_t, P]),
+}
+
+_libs = {}
+
+
+def load(host_only: bool = False) -> C.CDLL:
+    """The product library (libpa.so), or with ``host_only`` the g++ build of
+    the host manager alone (libpa_host.so).  The environment variable
+    PA_LIBRARY names another build of libpa.so (used when sweeping compile-
+    time launch parameters)."""
+    path = HOST_LIB_PATH if host_only else os.environ.get("PA_LIBRARY", LIB_PATH)
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{os.path.basename(path)} is not built: run "
+                           "`python -m paged_kv_cache_239_amd.build` first")
+    lib = C.CDLL(path)
+    sigs = dict(HOST_SIGNATURES)
+    if not host_only:
+        sigs.update(DEVICE_SIGNATURES)
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _libs[path] = lib
+    return lib
+
+
+def check(lib: C.CDLL, status: int, n_done: int = 0) -> None:
+    if status == PA_OK:
+        return
+    msg = lib.pa_last_error().decode(errors="replace")
+    if status == PA_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocks(status, msg, n_done)
+    raise PAError(status, msg, n_done)

@@ -1,0 +1,899 @@
+// Device side of the paged key/value cache for gfx950 (CDNA4, wave64):
+//   - write_kv     : scatter each new token's keys/values into its slot
+//   - copy_blocks  : whole-block copies for copy-on-write
+//   - decode attn  : single-query attention over block tables, split into
+//                    context partitions merged by the online-softmax rescale
+//
+// Sources (page title, section):
+//   "vLLM PagedAttention and continuous batching" -- "PagedAttention: fixed
+//     blocks, non-contiguous physical memory" (score one block, then the
+//     next, and combine; blocks need not be adjacent), "Sharing with
+//     reference counts and copy-on-write" (copy the one shared block before
+//     the write), "The kernel page, and what the 2023 runs measured" (one
+//     query token per sequence, separate key and value caches, compile-time
+//     block size), "How it works" (decode re-reads the whole cache every
+//     step and is memory-bound).
+//   "Serving Language Models Within a Memory Budget" -- section 6 (scaled
+//     scores, softmax, weighted values; extreme logits must not overflow)
+//     and eq. (4) (running maximum m' = max(m, max_j s_j), normaliser
+//     l' = e^(m-m') l + sum_j e^(s_j-m'), accumulator rescaled by the same
+//     factor).
+//   "PagedAttention and Online Inference" -- section 1 (grouped-query
+//     attention: several query heads read one key/value head).
+//
+// Kernel design (memory-bound: 2G flops per 2-byte key or value element):
+//   * One workgroup of NW wave64s per (sequence, key/value head, context
+//     partition).  The G query heads of the group are staged once in LDS and
+//     then held in registers as packed 16-bit pairs.
+//   * A wave consumes 16 tokens per step: four 16-byte loads per lane for K
+//     and four for V.  Lane = (row r = lane/16, chunk c = lane%16): load j
+//     reads token 4j+r, dims 8c..8c+7, so every load instruction covers 1 KiB
+//     of contiguous cache.  The next 16 tokens are in flight while the
+//     current ones are scored.
+//   * Scores: v_dot2 (fp16 or bf16 pairs, fp32 accumulation) gives 4G
+//     partial dot products per lane; a DPP reduce-scatter over the 16 lanes
+//     of a row (row_mirror, row_half_mirror, quad xor 2, quad xor 1) leaves
+//     each lane with complete scores of distinct (head, token) pairs, so
+//     each exponential is evaluated by one lane only.  The probabilities are
+//     exchanged through a small per-wave LDS buffer for the P.V products.
+//   * Online softmax per (row, head) in the base-2 domain (scale * log2 e
+//     folded into the scores).  The running maximum is raised only when a
+//     block's maximum exceeds it by more than 2^8; the kept weights are then
+//     at most 2^8 and the result is unchanged (numerator and denominator
+//     share the offset).
+//   * Partition end: rows combine with lane shuffles, waves through LDS.
+//     One partition: normalise and store.  Several: store (m, l, acc) to the
+//     workspace; a second, small kernel merges the partitions of every
+//     (sequence, head) by the eq. (4) rescale.  The kernel boundary makes the
+//     partials visible across the chip's L2 caches without a device-scope
+//     fence per workgroup (such a fence writes back a whole L2).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <string>
+
+#include "pa_internal.h"
+
+using pa_detail::fail;
+
+namespace {
+
+constexpr int kD = 128;            // head dimension of every compiled kernel
+constexpr int kRowBytes = kD * 2;  // one token of one head: 256 bytes
+constexpr float kRescaleSlack = 8.0f;  // log2 of the largest kept weight
+
+// Key/value tiles are read once per step: load them with the streaming
+// (non-temporal) hint so they do not displace reusable lines.
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1
+#endif
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal (streaming) cache hint
+__device__ __forceinline__ uint4 nt_load16(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ float dot8(const uint4 q, const uint4 k, float acc) {
+  if constexpr (BF16) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.x), __builtin_bit_cast(bf162_t, q.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.y), __builtin_bit_cast(bf162_t, q.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.z), __builtin_bit_cast(bf162_t, q.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.w), __builtin_bit_cast(bf162_t, q.w), acc, false);
+  } else {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.x), __builtin_bit_cast(half2_t, q.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.y), __builtin_bit_cast(half2_t, q.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.z), __builtin_bit_cast(half2_t, q.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.w), __builtin_bit_cast(half2_t, q.w), acc, false);
+  }
+  return acc;
+}
+
+// 8 packed 16-bit values -> 8 floats (exact)
+template <bool BF16>
+__device__ __forceinline__ void widen8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    } else {
+      const half2_t h = __builtin_bit_cast(half2_t, w[i]);
+      f[2 * i] = (float)h.x;
+      f[2 * i + 1] = (float)h.y;
+    }
+  }
+}
+
+// float -> 16-bit storage pattern, round to nearest even
+template <bool BF16>
+__device__ __forceinline__ uint32_t narrow1(float x) {
+  if constexpr (BF16) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+  } else {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint4 narrow8(const float (&f)[8]) {
+  uint4 r;
+  r.x = narrow1<BF16>(f[0]) | (narrow1<BF16>(f[1]) << 16);
+  r.y = narrow1<BF16>(f[2]) | (narrow1<BF16>(f[3]) << 16);
+  r.z = narrow1<BF16>(f[4]) | (narrow1<BF16>(f[5]) << 16);
+  r.w = narrow1<BF16>(f[6]) | (narrow1<BF16>(f[7]) << 16);
+  return r;
+}
+
+// DPP lane exchange inside a row of 16 lanes.  Every pattern used here is an
+// xor of the lane index: row_mirror = xor 15, row_half_mirror = xor 7,
+// quad_perm [2,3,0,1] = xor 2, quad_perm [1,0,3,2] = xor 1.
+constexpr int kDppMirror = 0x140;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppXor1 = 0xB1;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Stage k of the reduction over the 16 lanes of a row: partner = lane ^ mask_k
+// with mask = 15, 7, 2, 1; the partner differs in bit (3-k) and agrees on the
+// higher bits.
+template <int K> struct Stage;
+template <> struct Stage<0> { static constexpr int ctrl = kDppMirror;     static constexpr int bit = 3; };
+template <> struct Stage<1> { static constexpr int ctrl = kDppHalfMirror; static constexpr int bit = 2; };
+template <> struct Stage<2> { static constexpr int ctrl = kDppXor2;       static constexpr int bit = 1; };
+template <> struct Stage<3> { static constexpr int ctrl = kDppXor1;       static constexpr int bit = 0; };
+
+// One reduce-scatter stage: NV values per lane -> NV/2, each now summed over
+// the lane and its partner.  The lane keeps the half selected by its bit.
+template <int NV, int K>
+__device__ __forceinline__ void rs_stage(float* x, int c) {
+  const bool hi = (c >> Stage<K>::bit) & 1;
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const float lo = x[i], up = x[i + NV / 2];
+    const float keep = hi ? up : lo;
+    const float send = hi ? lo : up;
+    x[i] = keep + dpp<Stage<K>::ctrl>(send);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void ar_stage(float* x) {
+  x[0] = x[0] + dpp<Stage<K>::ctrl>(x[0]);
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Per GQA group size G: the 4G partial dot products of a lane (index
+// v = 4h + j: head h, load j) are summed over the 16 lanes of the row.
+// Afterwards lane c holds E = max(1, 4G/16) complete scores with indices
+// value_index(c, e).
+template <int G>
+struct Scores {
+  static constexpr int NV = 4 * G;
+  static constexpr int LOGNV = ilog2(NV);
+  static constexpr int NRS = LOGNV < 4 ? LOGNV : 4;   // reduce-scatter stages
+  static constexpr int E = NV >> NRS;                  // scores left per lane
+  static constexpr int LANES_PER_HEAD = 16 / G;        // lanes of a row owning one head
+
+  __device__ static __forceinline__ void reduce(float (&x)[NV], int c) {
+    if constexpr (NRS >= 1) rs_stage<NV, 0>(x, c); else ar_stage<0>(x);
+    if constexpr (NRS >= 2) rs_stage<NV / 2, 1>(x, c); else ar_stage<1>(x);
+    if constexpr (NRS >= 3) rs_stage<NV / 4, 2>(x, c); else ar_stage<2>(x);
+    if constexpr (NRS >= 4) rs_stage<NV / 8, 3>(x, c); else ar_stage<3>(x);
+  }
+  __device__ static __forceinline__ int value_index(int c, int e) {
+    return ((c >> (4 - NRS)) << (LOGNV - NRS)) + e;
+  }
+  // max / sum over the lanes of a row that hold the same head but other tokens
+  template <bool MAX>
+  __device__ static __forceinline__ float across_tokens(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (G == 1) {        // tokens on lane bits 3,2
+      x = op(x, dpp<kDppMirror>(x));
+      x = op(x, dpp<kDppHalfMirror>(x));
+    } else if constexpr (G == 2) { // tokens on lane bits 2,1
+      x = op(x, dpp<kDppXor2>(x));
+      x = op(x, dpp<kDppHalfMirror>(x));
+    } else if constexpr (G == 4) { // tokens on lane bits 1,0
+      x = op(x, dpp<kDppXor1>(x));
+      x = op(x, dpp<kDppXor2>(x));
+    } else {                       // G == 8: tokens on lane bit 0 (and e)
+      x = op(x, dpp<kDppXor1>(x));
+    }
+    return x;
+  }
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// decode attention
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const char* kslab;        // layer's key slab   [P][Hkv][B][d]
+  const char* vslab;        // layer's value slab [P][Hkv][B][d]
+  uint64_t tile_bytes;      // Hkv * B * d * 2: stride of one physical block
+  const uint16_t* q;        // [S][Hq][d]
+  uint16_t* out;            // [S][Hq][d]
+  const int32_t* tables;    // [S][maxb]
+  const int32_t* lens;      // [S]
+  float* ws_ml;             // [S][Hkv][nparts_max][G][2]  (max, normaliser)
+  float* ws_acc;            // [S][Hkv][nparts_max][G][d]
+  int S, Hq, Hkv, P, maxb, max_ctx, part_tokens, nparts_max;
+  int grid_order;           // see decode_attention_kernel
+  int pstride;              // partitions per (sequence, head) in grid order 1
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+#ifdef PA_WAVES_PER_EU
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_OCCUPANCY
+#endif
+
+template <bool BF16, int G, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a) {
+  using SC = Scores<G>;
+  constexpr int E = SC::E;
+  static_assert(BS % 16 == 0, "a 16-token step must stay inside one block");
+
+  // 1-D grid; the dispatcher deals consecutive workgroups round-robin to the
+  // 8 XCDs, so the order decides each XCD's share of the work.
+  //   order 0: head fastest -- XCD = head mod 8 when 8 | Hkv, an equal share
+  //            of every sequence for every XCD;
+  //   order 1: partition fastest with an odd partition stride, so the
+  //            partitions of one (sequence, head) spread over all XCDs.
+  int kvh, s, p;
+  {
+    const uint32_t id = blockIdx.x;
+    if (a.grid_order == 0) {
+      kvh = id % a.Hkv;
+      const uint32_t t = id / a.Hkv;
+      s = t % a.S;
+      p = t / a.S;
+    } else {
+      p = id % a.pstride;
+      const uint32_t t = id / a.pstride;
+      kvh = t % a.Hkv;
+      s = t / a.Hkv;
+    }
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4;   // row: token offset inside a 4-token load
+  const int c = lane & 15;   // 16-byte chunk: dims 8c..8c+7
+
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  n = __builtin_amdgcn_readfirstlane(n);
+  const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
+  if (p >= nparts) return;
+  const int t_begin = p * a.part_tokens;
+  const int t_end = min(n, t_begin + a.part_tokens);
+
+  __shared__ uint4 s_q[G * 16];
+  __shared__ __attribute__((aligned(16))) float s_p[NW][2][4][4 * G];
+  __shared__ float s_f[NW][4][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[NW][G][kD];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
+  const uint32_t lane_off = (uint32_t)(r * kRowBytes + c * 16);
+
+  // running state of this lane's (row, head)
+  float m = -INFINITY;
+  float ell = 0.0f;
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
+
+  int hown;  // head owned by this lane after the reduction
+  {
+    const int v0 = SC::value_index(c, 0);
+    hown = v0 >> 2;
+  }
+
+  // groups of 16 tokens in this partition, dealt round-robin to the waves:
+  // the k-th group of this wave is g_first + k * NW.  Lane k holds that
+  // group's physical block (read once here; a lane read per group later).
+  const int g_first = t_begin / 16 + wave;
+  const int g_full = t_end / 16;               // groups [.., g_full) are full
+  const int g_last = (t_end + 15) / 16;        // a tail group exists if g_full < g_last
+
+  // The query group (G heads x 256 bytes) and the block-table entries are
+  // requested together; the query is staged through LDS only after the
+  // first key/value loads are in flight.
+  const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
+  uint4 qr[G];
+  int my_phys = 0;
+  {
+    const int g = g_first + lane * NW;
+    if (g < g_last) {
+      const int e = table[(g * 16) / BS];
+      my_phys = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+    }
+  }
+
+  auto load_group = [&](int k, uint4 (&K)[4], uint4 (&V)[4], bool tail) {
+    const int g = g_first + k * NW;
+    const int tok0 = g * 16;
+    const int phys = __builtin_amdgcn_readlane(my_phys, k);
+    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok0 % BS) * kRowBytes;
+    const char* kb = a.kslab + off;
+    const char* vb = a.vslab + off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!tail || tok0 + 4 * j < n) {
+#if PA_NT_LOADS
+        K[j] = nt_load16(kb + j * 4 * kRowBytes + lane_off);
+        V[j] = nt_load16(vb + j * 4 * kRowBytes + lane_off);
+#else
+        K[j] = *reinterpret_cast<const uint4*>(kb + j * 4 * kRowBytes + lane_off);
+        V[j] = *reinterpret_cast<const uint4*>(vb + j * 4 * kRowBytes + lane_off);
+#endif
+      } else {
+        K[j] = make_uint4(0, 0, 0, 0);
+        V[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int buf = 0;
+  auto process_group = [&](int g, const uint4 (&K)[4], const uint4 (&V)[4], bool tail) {
+    const int tok0 = g * 16;
+    // partial dot products: x[4h + j] = q_h . k(token 4j + r) over this lane's 8 dims
+    float x[4 * G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * h + j] = dot8<BF16>(qr[h], K[j], 0.0f);
+    SC::reduce(x, c);
+
+    float sc[E];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sc[e] = x[e] * a.scale_log2;
+      if (tail) {
+        const int j = SC::value_index(c, e) & 3;
+        if (tok0 + 4 * j + r >= n) sc[e] = -INFINITY;
+      }
+      mx = fmaxf(mx, sc[e]);
+    }
+    mx = SC::template across_tokens<true>(mx);
+
+    // raise the running maximum only when the block would exceed it by > 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float f = (m_new == m) ? 1.0f : exp2_fast(m - m_new);
+      m = m_new;
+      ell *= f;
+      s_f[wave][r][hown] = f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float fh = s_f[wave][r][h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] *= fh;
+      }
+    }
+
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float pe = (tail && sc[e] == -INFINITY) ? 0.0f : exp2_fast(sc[e] - m);
+      ell += pe;
+      s_p[wave][buf][r][SC::value_index(c, e)] = pe;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float pv[4 * G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float4 t = *reinterpret_cast<const float4*>(&s_p[wave][buf][r][4 * i]);
+      pv[4 * i] = t.x; pv[4 * i + 1] = t.y; pv[4 * i + 2] = t.z; pv[4 * i + 3] = t.w;
+    }
+    buf ^= 1;
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float vf[8];
+      widen8<BF16>(V[j], vf);
+      if (tail && tok0 + 4 * j + r >= n) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vf[i] = 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float w = pv[4 * h + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(w, vf[i], acc[h][i]);
+      }
+    }
+  };
+
+  {
+    // Two register buffers; the next group's loads are issued before the
+    // current group is scored.  The prefetch index is clamped instead of
+    // skipped, so every path through the loop has the same loads in flight
+    // and the wait before scoring covers exactly the current group.
+    const int ng = g_full > g_first ? (g_full - g_first + NW - 1) / NW : 0;
+    uint4 K0[4], V0[4], K1[4], V1[4];
+    // unconditional, so that every path has the same loads in flight (a wave
+    // without a full group reads an in-bounds stand-in block and ignores it)
+    load_group(0, K0, V0, false);
+    if (threadIdx.x < G * 16) s_q[threadIdx.x] = qv;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) qr[h] = s_q[h * 16 + c];
+    if (ng > 0) {
+      // invariant at the top of every iteration: buffer 0 holds group k's
+      // loads (issued, maybe not complete) and nothing else is in flight
+      int k = 0;
+      for (; k + 2 < ng; k += 2) {
+        load_group(k + 1, K1, V1, false);
+        process_group(g_first + k * NW, K0, V0, false);
+        load_group(k + 2, K0, V0, false);
+        process_group(g_first + (k + 1) * NW, K1, V1, false);
+      }
+      // the last one or two groups: no loads beyond this wave's groups
+      if (k + 2 == ng) {
+        load_group(k + 1, K1, V1, false);
+        process_group(g_first + k * NW, K0, V0, false);
+        process_group(g_first + (k + 1) * NW, K1, V1, false);
+      } else {
+        process_group(g_first + k * NW, K0, V0, false);
+      }
+    }
+    if (g_full < g_last && g_full >= g_first && (g_full - g_first) % NW == 0) {
+      const int kt = (g_full - g_first) / NW;
+      load_group(kt, K0, V0, true);
+      process_group(g_full, K0, V0, true);
+    }
+  }
+
+  // ---- combine: tokens of a row, then rows, then waves ---------------------
+  ell = SC::template across_tokens<false>(ell);
+  float mh[G], lh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int owner = (lane & 0x30) | (h * SC::LANES_PER_HEAD);
+    mh[h] = __shfl(m, owner);
+    lh[h] = __shfl(ell, owner);
+  }
+#pragma unroll
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(mh[h], sh);
+      const float lo = __shfl_xor(lh[h], sh);
+      const float M = fmaxf(mh[h], mo);
+      const float wa = (mh[h] == -INFINITY) ? 0.0f : exp2_fast(mh[h] - M);
+      const float wb = (mo == -INFINITY) ? 0.0f : exp2_fast(mo - M);
+      lh[h] = wa * lh[h] + wb * lo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = wa * acc[h][i] + wb * __shfl_xor(acc[h][i], sh);
+      mh[h] = M;
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&s_acc[wave][h][8 * c]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_m[wave][h] = mh[h];
+        s_l[wave][h] = lh[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  const bool worker = t < G * 16;     // one thread per (head, 8-dim chunk)
+  const int wh = t >> 4;
+  const int wc = t & 15;
+  float A[8];
+  float M = -INFINITY, Lsum = 0.0f;
+  if (worker) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][wh]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_m[w][wh];
+      const float wt = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
+      Lsum += wt * s_l[w][wh];
+      const float4 a0 = *reinterpret_cast<const float4*>(&s_acc[w][wh][8 * wc]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s_acc[w][wh][8 * wc + 4]);
+      A[0] += wt * a0.x; A[1] += wt * a0.y; A[2] += wt * a0.z; A[3] += wt * a0.w;
+      A[4] += wt * a1.x; A[5] += wt * a1.y; A[6] += wt * a1.z; A[7] += wt * a1.w;
+    }
+  }
+
+  uint4* out_row = reinterpret_cast<uint4*>(a.out + ((size_t)s * a.Hq + (size_t)kvh * G + wh) * kD) + wc;
+  if (nparts == 1) {
+    if (worker) {
+      const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = A[i] * inv;
+      *out_row = narrow8<BF16>(o);
+    }
+    return;
+  }
+
+  // ---- several partitions: store this partition's (m, l, acc) --------------
+  if (worker) {
+    const size_t pbase = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
+    float4* dst = reinterpret_cast<float4*>(a.ws_acc + ((pbase + p) * G + wh) * kD + 8 * wc);
+    dst[0] = make_float4(A[0], A[1], A[2], A[3]);
+    dst[1] = make_float4(A[4], A[5], A[6], A[7]);
+    if (wc == 0) *reinterpret_cast<float2*>(a.ws_ml + ((pbase + p) * G + wh) * 2) = make_float2(M, Lsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of the context partitions (eq. (4) rescale): one wave per
+// (sequence, key/value head); thread = (head, 8-dim chunk)
+// ---------------------------------------------------------------------------
+template <bool BF16, int G>
+__global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a) {
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
+  if (nparts <= 1) return;  // written directly by the partition kernel
+  const int wh = threadIdx.x >> 4;
+  const int wc = threadIdx.x & 15;
+  const size_t pbase = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
+  // online merge over partitions, CHUNK at a time so the loads of a chunk
+  // are all in flight together
+  constexpr int CHUNK = 4;
+  float Mg = -INFINITY, Lg = 0.0f, Ag[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Ag[i] = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += CHUNK) {
+    float2 ml[CHUNK];
+    float4 x0[CHUNK], x1[CHUNK];
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) {
+      const int pp = p0 + k < nparts ? p0 + k : nparts - 1;
+      ml[k] = *reinterpret_cast<const float2*>(a.ws_ml + ((pbase + pp) * G + wh) * 2);
+      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + ((pbase + pp) * G + wh) * kD + 8 * wc);
+      x0[k] = src[0];
+      x1[k] = src[1];
+    }
+    float mc = Mg;
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k)
+      if (p0 + k < nparts) mc = fmaxf(mc, ml[k].x);
+    const float f = (Mg == -INFINITY) ? 0.0f : exp2_fast(Mg - mc);
+    Lg *= f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Ag[i] *= f;
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) {
+      if (p0 + k >= nparts) break;
+      const float wt = (ml[k].x == -INFINITY) ? 0.0f : exp2_fast(ml[k].x - mc);
+      Lg += wt * ml[k].y;
+      Ag[0] += wt * x0[k].x; Ag[1] += wt * x0[k].y; Ag[2] += wt * x0[k].z; Ag[3] += wt * x0[k].w;
+      Ag[4] += wt * x1[k].x; Ag[5] += wt * x1[k].y; Ag[6] += wt * x1[k].z; Ag[7] += wt * x1[k].w;
+    }
+    Mg = mc;
+  }
+  const float inv = Lg > 0.0f ? 1.0f / Lg : 0.0f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = Ag[i] * inv;
+  uint4* out_row = reinterpret_cast<uint4*>(a.out + ((size_t)s * a.Hq + (size_t)kvh * G + wh) * kD) + wc;
+  *out_row = narrow8<BF16>(o);
+}
+
+// ---------------------------------------------------------------------------
+// write_kv: one workgroup per token
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void write_kv_kernel(char* kslab, char* vslab, const uint4* k, const uint4* v,
+                                                       const int64_t* slots, int Hkv, int B, int64_t nslots,
+                                                       uint64_t tile_bytes) {
+  const int s = blockIdx.x;
+  const int64_t slot = slots[s];
+  if (slot < 0 || slot >= nslots) return;
+  const int64_t blk = slot / B;
+  const int off = (int)(slot % B);
+  const int chunks_per_row = kRowBytes / 16;  // 16
+  const int chunks = Hkv * chunks_per_row;
+  for (int i = threadIdx.x; i < chunks; i += blockDim.x) {
+    const int h = i / chunks_per_row;
+    const int w = i % chunks_per_row;
+    const uint64_t dst = (uint64_t)blk * tile_bytes + ((uint64_t)h * B + off) * kRowBytes + (uint64_t)w * 16;
+    *reinterpret_cast<uint4*>(kslab + dst) = k[(size_t)s * chunks + i];
+    *reinterpret_cast<uint4*>(vslab + dst) = v[(size_t)s * chunks + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// copy_blocks: grid (chunk groups, 2L slabs, pairs)
+// ---------------------------------------------------------------------------
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* base, const int32_t* pairs, int P,
+                                                          uint64_t tile_bytes, uint64_t slab_bytes) {
+  const int pr = blockIdx.z;
+  const int32_t src = pairs[2 * pr];
+  const int32_t dst = pairs[2 * pr + 1];
+  if (src < 0 || src >= P || dst < 0 || dst >= P || src == dst) return;
+  char* slab = base + (uint64_t)blockIdx.y * slab_bytes;
+  const uint4* from = reinterpret_cast<const uint4*>(slab + (uint64_t)src * tile_bytes);
+  uint4* to = reinterpret_cast<uint4*>(slab + (uint64_t)dst * tile_bytes);
+  const uint64_t nchunks = tile_bytes / 16;
+  const uint64_t first = (uint64_t)blockIdx.x * (256 * kCopyUnroll) + threadIdx.x;
+  uint4 tmp[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const uint64_t i = first + (uint64_t)u * 256;
+    if (i < nchunks) tmp[u] = from[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const uint64_t i = first + (uint64_t)u * 256;
+    if (i < nchunks) to[i] = tmp[u];
+  }
+}
+
+__global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntail) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t k = i; k < n16; k += stride) p[k] = make_uint4(0, 0, 0, 0);
+  if (i < ntail) tail[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch configuration
+// ---------------------------------------------------------------------------
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+constexpr int kWaves = PA_WAVES;  // waves per workgroup
+
+struct LaunchCfg {
+  int part_tokens = 0;
+  int nparts_max = 1;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+// Partition length: as long as possible (fewer partials to merge) while the
+// grid still has several workgroups per compute unit.
+LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
+  static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
+  int gpw = 16;
+  if (forced > 0) {
+    gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
+  } else {
+    const int64_t target = 2048;  // workgroups: 256 CUs x 8
+    while (gpw > 1) {
+      const int64_t part = 16LL * kWaves * gpw;
+      const int64_t wgs = (int64_t)S * Hkv * ((max_ctx + part - 1) / part);
+      if (wgs >= target) break;
+      gpw /= 2;
+    }
+  }
+  LaunchCfg cfg;
+  cfg.part_tokens = 16 * kWaves * gpw;
+  cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
+  return cfg;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t ml_off = 0, acc_off = 0, total = 0;
+};
+
+WsLayout ws_layout(int S, int Hkv, int G, const LaunchCfg& cfg) {
+  WsLayout w;
+  if (cfg.nparts_max <= 1) return w;
+  const size_t units = (size_t)S * Hkv;
+  w.ml_off = 0;
+  w.acc_off = w.ml_off + align_up(units * cfg.nparts_max * G * 2 * sizeof(float), 256);
+  w.total = w.acc_off + align_up(units * cfg.nparts_max * G * kD * sizeof(float), 256);
+  return w;
+}
+
+pa_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <bool BF16, int G, int BS>
+void launch_decode(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
+  if (args.nparts_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, G>), dim3(args.Hkv, args.S), dim3(G * 16), 0, stream, args);
+}
+
+template <bool BF16, int BS>
+bool dispatch_g(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_decode<BF16, 1, BS>(args, grid, stream); return true;
+    case 2: launch_decode<BF16, 2, BS>(args, grid, stream); return true;
+    case 4: launch_decode<BF16, 4, BS>(args, grid, stream); return true;
+    case 8: launch_decode<BF16, 8, BS>(args, grid, stream); return true;
+    default: return false;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v, const int64_t* slot_mapping, int S,
+                      hipStream_t stream) {
+  pa_detail::clear_error();
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
+  if (S == 0) return PA_OK;
+  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
+  if (S > 2147483647) return fail(PA_ERR_INVALID_ARG, "S too large");
+  hipLaunchKernelGGL(write_kv_kernel, dim3(S), dim3(256), 0, stream, pool->k_slab(layer), pool->v_slab(layer),
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping, pool->Hkv, pool->B,
+                     (int64_t)pool->P * pool->B, (uint64_t)pool->tile_bytes);
+  return hip_check(hipGetLastError(), "write_kv launch");
+}
+
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (N < 0) return fail(PA_ERR_INVALID_ARG, "negative N");
+  if (N == 0) return PA_OK;
+  if (!pairs || !aligned(pairs, 4)) return fail(PA_ERR_INVALID_ARG, "pairs must be a 4-byte aligned device pointer");
+  if (N > 65535) return fail(PA_ERR_INVALID_ARG, "at most 65535 pairs per call");
+  if (2 * pool->L > 65535) return fail(PA_ERR_UNSUPPORTED, "too many layers");
+  if (pool->tile_bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block size in bytes must be a multiple of 16");
+  const uint64_t nchunks = pool->tile_bytes / 16;
+  const uint64_t per_wg = 256 * kCopyUnroll;
+  const dim3 grid((unsigned)((nchunks + per_wg - 1) / per_wg), (unsigned)(2 * pool->L), (unsigned)N);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, pool->base, pairs, pool->P,
+                     (uint64_t)pool->tile_bytes, (uint64_t)pool->slab_bytes);
+  return hip_check(hipGetLastError(), "copy_blocks launch");
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx) {
+  if (!pool || S <= 0 || Hq <= 0 || max_ctx < 0 || Hq % pool->Hkv) return 0;
+  // Sized for the shortest partition the launcher can pick, so the result
+  // never decreases with S or max_ctx and one allocation serves every call
+  // up to these sizes.
+  LaunchCfg cfg;
+  cfg.part_tokens = 16 * kWaves;
+  cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
+  if (cfg.nparts_max <= 1 && max_ctx > 0) cfg.nparts_max = 2;
+  return ws_layout(S, pool->Hkv, Hq / pool->Hkv, cfg).total;
+}
+
+pa_status pa_decode_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (ws_bytes == 0) return PA_OK;
+  if (!workspace || !aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const uint64_t n16 = ws_bytes / 16;
+  const uint64_t ntail = ws_bytes % 16;
+  uint64_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4*>(workspace), n16,
+                     static_cast<uint8_t*>(workspace) + n16 * 16, ntail);
+  return hip_check(hipGetLastError(), "workspace init launch");
+}
+
+pa_status pa_decode_attention(pa_pool* pool, int layer, void* out, const void* q, int S, int Hq,
+                              const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx,
+                              float scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
+  if (S == 0) return PA_OK;
+  if (Hq <= 0 || Hq % pool->Hkv) return fail(PA_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+  const int G = Hq / pool->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
+  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
+  if (pool->B != 16 && pool->B != 32) return fail(PA_ERR_UNSUPPORTED, "block size must be 16 or 32");
+  if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
+  if (maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad maxb or max_ctx");
+  if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
+
+  const LaunchCfg cfg = choose_launch(S, pool->Hkv, max_ctx);
+  const WsLayout wl = ws_layout(S, pool->Hkv, G, cfg);
+  char* ws = static_cast<char*>(workspace);
+  if (wl.total > 0) {
+    if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+    if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_workspace_bytes");
+  }
+
+  DecodeArgs args;
+  args.kslab = pool->k_slab(layer);
+  args.vslab = pool->v_slab(layer);
+  args.tile_bytes = pool->tile_bytes;
+  args.q = static_cast<const uint16_t*>(q);
+  args.out = static_cast<uint16_t*>(out);
+  args.tables = block_tables;
+  args.lens = context_lens;
+  args.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+  args.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+  args.S = S;
+  args.Hq = Hq;
+  args.Hkv = pool->Hkv;
+  args.P = pool->P;
+  args.maxb = maxb;
+  args.max_ctx = max_ctx;
+  args.part_tokens = cfg.part_tokens;
+  args.nparts_max = cfg.nparts_max;
+  args.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+  static const int grid_order = env_int("PA_GRID_ORDER", 0) == 1 ? 1 : 0;
+  args.grid_order = grid_order;
+  args.pstride = cfg.nparts_max | 1;
+  const uint64_t nwg = (uint64_t)pool->Hkv * S * (grid_order == 0 ? cfg.nparts_max : args.pstride);
+  if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const dim3 grid((unsigned)nwg);
+  bool ok;
+  const bool bf16 = pool->dtype == PA_BF16;
+  if (pool->B == 16)
+    ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream);
+  else
+    ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream);
+  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+  return hip_check(hipGetLastError(), "decode attention launch");
+}
+
+}  // extern "C"

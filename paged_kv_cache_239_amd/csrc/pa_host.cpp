@@ -1,0 +1,403 @@
+// Pool carving and the host block manager: FIFO free list, per-block
+// reference counts, fork / append / free and the copy-on-write decision.
+//
+// Sources ("vLLM PagedAttention and continuous batching", netleverage.com):
+//   section "PagedAttention: fixed blocks, non-contiguous physical memory" --
+//     one contiguous device allocation sliced into physical blocks; a block
+//     table per sequence filled left to right; a new block only when the
+//     previous one is full;
+//   section "Sharing with reference counts and copy-on-write" -- refcounts,
+//     copy of a shared block on write, release at count zero, the fork /
+//     append / free policies.
+// Readings where the pages are silent: FIFO free list seeded by a caller
+// permutation (release appends at the tail, which keeps a freed address out
+// of circulation for as long as possible); batch order decides which of
+// several sharers copies (every writer that finds count > 1 copies, the one
+// that finds count == 1 writes in place).
+//
+// Pure host C++ (no HIP), so it also builds with g++ alone for host tests.
+
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace pa_detail {
+
+static thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace pa_detail
+
+using pa_detail::fail;
+
+namespace {
+
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > std::numeric_limits<size_t>::max() / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Bytes of one layer's K (or V) slab; false on overflow or bad arguments.
+bool slab_size(int Hkv, int d, int B, int P, size_t* tile, size_t* slab) {
+  if (Hkv <= 0 || d <= 0 || B <= 0 || P <= 0) return false;
+  size_t t = 2;
+  if (!mul_ok(t, (size_t)Hkv, &t) || !mul_ok(t, (size_t)B, &t) || !mul_ok(t, (size_t)d, &t))
+    return false;
+  size_t s;
+  if (!mul_ok(t, (size_t)P, &s)) return false;
+  *tile = t;
+  *slab = s;
+  return true;
+}
+
+pa_status check_pool(const pa_pool* pool) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  return PA_OK;
+}
+
+bool in_range(const pa_pool* pool, int32_t blk) { return blk >= 0 && blk < pool->P; }
+
+// --- FIFO free list --------------------------------------------------------
+int32_t fifo_pop(pa_pool* pool) {
+  int32_t blk = pool->ring[(size_t)pool->head];
+  pool->head = (pool->head + 1) % pool->P;
+  pool->nfree -= 1;
+  return blk;
+}
+
+void fifo_push(pa_pool* pool, int32_t blk) {
+  int64_t tail = (pool->head + pool->nfree) % pool->P;
+  pool->ring[(size_t)tail] = blk;
+  pool->nfree += 1;
+}
+
+// --- primitives (arguments already validated) --------------------------------
+int32_t do_alloc(pa_pool* pool) {
+  int32_t blk = fifo_pop(pool);
+  pool->ref[(size_t)blk] = 1;
+  pool->allocs += 1;
+  int32_t live = pool->P - pool->nfree;
+  if (live > pool->live_high_water) pool->live_high_water = live;
+  return blk;
+}
+
+void do_decref(pa_pool* pool, int32_t blk) {
+  int32_t& r = pool->ref[(size_t)blk];
+  r -= 1;
+  if (r == 0) {
+    fifo_push(pool, blk);
+    pool->releases += 1;
+  }
+}
+
+// One append; the a1 rule.  Leaves everything unchanged on error.
+pa_status do_append(pa_pool* pool, int32_t* table, int32_t maxb, int32_t n_before,
+                    int64_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  *cow_src = -1;
+  *cow_dst = -1;
+  if (n_before < 0) return fail(PA_ERR_INVALID_ARG, "negative sequence length");
+  const int32_t idx = n_before / pool->B;
+  const int32_t off = n_before % pool->B;
+  if (idx >= maxb) return fail(PA_ERR_INVALID_ARG, "block table too short for the new token");
+  if (off == 0) {
+    if (pool->nfree == 0) return fail(PA_ERR_OUT_OF_BLOCKS, "no free physical block");
+    const int32_t blk = do_alloc(pool);
+    table[idx] = blk;
+    *slot = (int64_t)blk * pool->B;
+    return PA_OK;
+  }
+  const int32_t last = table[idx];
+  if (!in_range(pool, last)) return fail(PA_ERR_INVALID_ARG, "table entry outside the pool");
+  if (pool->ref[(size_t)last] == 0) return fail(PA_ERR_INVALID_ARG, "table maps a free block");
+  if (pool->ref[(size_t)last] > 1) {
+    if (pool->nfree == 0) return fail(PA_ERR_OUT_OF_BLOCKS, "no free block for copy-on-write");
+    const int32_t fresh = do_alloc(pool);
+    do_decref(pool, last);  // count was > 1, so the old block stays live
+    table[idx] = fresh;
+    pool->cows += 1;
+    *cow_src = last;
+    *cow_dst = fresh;
+    *slot = (int64_t)fresh * pool->B + off;
+    return PA_OK;
+  }
+  *slot = (int64_t)last * pool->B + off;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa_detail::g_last_error.c_str(); }
+
+const char* pa_version(void) { return "pa 0.1.0 gfx950"; }
+
+size_t pa_pool_bytes(int L, int Hkv, int d, int B, int P, pa_dtype dtype) {
+  if (L <= 0 || (dtype != PA_F16 && dtype != PA_BF16)) return 0;
+  size_t tile, slab, total;
+  if (!slab_size(Hkv, d, B, P, &tile, &slab)) return 0;
+  if (!mul_ok(slab, (size_t)2 * (size_t)L, &total)) return 0;
+  return total;
+}
+
+pa_status pa_alloc_pool(pa_pool** out, int L, int Hkv, int d, int B, int P, pa_dtype dtype,
+                        void* dev_base, size_t dev_bytes, const int32_t* free_order) {
+  pa_detail::clear_error();
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (L <= 0) return fail(PA_ERR_INVALID_ARG, "L must be positive");
+  size_t tile, slab;
+  if (!slab_size(Hkv, d, B, P, &tile, &slab))
+    return fail(PA_ERR_INVALID_ARG, "Hkv, d, B and P must be positive and their product must fit");
+  const size_t need = pa_pool_bytes(L, Hkv, d, B, P, dtype);
+  if (need == 0) return fail(PA_ERR_INVALID_ARG, "pool size overflows");
+  if (!dev_base) return fail(PA_ERR_INVALID_ARG, "dev_base is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_base) % 256 != 0)
+    return fail(PA_ERR_INVALID_ARG, "dev_base must be 256-byte aligned");
+  if (dev_bytes < need) return fail(PA_ERR_INVALID_ARG, "device buffer smaller than pa_pool_bytes");
+
+  pa_pool* pool = new (std::nothrow) pa_pool();
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+  pool->L = L;
+  pool->Hkv = Hkv;
+  pool->d = d;
+  pool->B = B;
+  pool->P = P;
+  pool->dtype = dtype;
+  pool->base = static_cast<char*>(dev_base);
+  pool->bytes = dev_bytes;
+  pool->tile_bytes = tile;
+  pool->slab_bytes = slab;
+  try {
+    pool->ref.assign((size_t)P, 0);
+    pool->ring.assign((size_t)P, 0);
+  } catch (...) {
+    delete pool;
+    return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+  }
+  if (free_order) {
+    std::vector<char> seen((size_t)P, 0);
+    for (int i = 0; i < P; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= P || seen[(size_t)b]) {
+        delete pool;
+        return fail(PA_ERR_INVALID_ARG, "free_order is not a permutation of 0..P-1");
+      }
+      seen[(size_t)b] = 1;
+      pool->ring[(size_t)i] = b;
+    }
+  } else {
+    for (int i = 0; i < P; ++i) pool->ring[(size_t)i] = i;
+  }
+  pool->head = 0;
+  pool->nfree = P;
+  *out = pool;
+  return PA_OK;
+}
+
+void pa_free_pool(pa_pool* pool) { delete pool; }
+
+pa_status pa_pool_layer_ptrs(const pa_pool* pool, int layer, void** k_slab, void** v_slab) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (k_slab) *k_slab = pool->k_slab(layer);
+  if (v_slab) *v_slab = pool->v_slab(layer);
+  return PA_OK;
+}
+
+pa_status pa_block_alloc(pa_pool* pool, int32_t* blk) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (!blk) return fail(PA_ERR_INVALID_ARG, "blk is NULL");
+  if (pool->nfree == 0) return fail(PA_ERR_OUT_OF_BLOCKS, "no free physical block");
+  *blk = do_alloc(pool);
+  return PA_OK;
+}
+
+pa_status pa_block_incref(pa_pool* pool, int32_t blk) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (!in_range(pool, blk)) return fail(PA_ERR_INVALID_ARG, "block outside the pool");
+  if (pool->ref[(size_t)blk] == 0) return fail(PA_ERR_INVALID_ARG, "incref of a free block");
+  pool->ref[(size_t)blk] += 1;
+  return PA_OK;
+}
+
+pa_status pa_block_decref(pa_pool* pool, int32_t blk) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (!in_range(pool, blk)) return fail(PA_ERR_INVALID_ARG, "block outside the pool");
+  if (pool->ref[(size_t)blk] == 0) return fail(PA_ERR_INVALID_ARG, "decref of a free block (double free)");
+  do_decref(pool, blk);
+  return PA_OK;
+}
+
+int32_t pa_block_refcount(const pa_pool* pool, int32_t blk) {
+  if (!pool || !in_range(pool, blk)) return -1;
+  return pool->ref[(size_t)blk];
+}
+
+int32_t pa_num_free_blocks(const pa_pool* pool) { return pool ? pool->nfree : -1; }
+
+pa_status pa_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* count) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (count) *count = pool->nfree;
+  if (!out && cap > 0) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+  const int32_t n = pool->nfree < cap ? pool->nfree : cap;
+  for (int32_t i = 0; i < n; ++i) out[i] = pool->ring[(size_t)((pool->head + i) % pool->P)];
+  return PA_OK;
+}
+
+pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (!stats) return fail(PA_ERR_INVALID_ARG, "stats is NULL");
+  stats->allocs = pool->allocs;
+  stats->cows = pool->cows;
+  stats->releases = pool->releases;
+  stats->live_blocks = pool->P - pool->nfree;
+  stats->live_high_water = pool->live_high_water;
+  stats->free_blocks = pool->nfree;
+  stats->num_blocks = pool->P;
+  return PA_OK;
+}
+
+pa_status pa_append_slot(pa_pool* pool, int32_t* table, int32_t maxb, int32_t n_before,
+                         int64_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (!table || !slot || !cow_src || !cow_dst) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  if (maxb <= 0) return fail(PA_ERR_INVALID_ARG, "maxb must be positive");
+  return do_append(pool, table, maxb, n_before, slot, cow_src, cow_dst);
+}
+
+pa_status pa_append_tokens(pa_pool* pool, int32_t* table, int32_t maxb, int32_t n_before,
+                           int32_t count, int64_t* slots, int32_t* cow_pairs, int32_t* n_pairs,
+                           int32_t* n_done) {
+  pa_detail::clear_error();
+  if (n_pairs) *n_pairs = 0;
+  if (n_done) *n_done = 0;
+  if (pa_status st = check_pool(pool)) return st;
+  if (!table) return fail(PA_ERR_INVALID_ARG, "table is NULL");
+  if (maxb <= 0 || count < 0 || n_before < 0)
+    return fail(PA_ERR_INVALID_ARG, "bad maxb, count or n_before");
+  if ((int64_t)n_before + count > (int64_t)std::numeric_limits<int32_t>::max())
+    return fail(PA_ERR_INVALID_ARG, "length overflows int32");
+  int32_t pairs = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    int64_t slot;
+    int32_t src, dst;
+    pa_status st = do_append(pool, table, maxb, n_before + i, &slot, &src, &dst);
+    if (st != PA_OK) {
+      if (n_done) *n_done = i;
+      if (n_pairs) *n_pairs = pairs;
+      return st;
+    }
+    if (slots) slots[i] = slot;
+    if (src >= 0) {
+      if (cow_pairs) {
+        cow_pairs[2 * pairs] = src;
+        cow_pairs[2 * pairs + 1] = dst;
+      }
+      pairs += 1;
+    }
+  }
+  if (n_done) *n_done = count;
+  if (n_pairs) *n_pairs = pairs;
+  return PA_OK;
+}
+
+pa_status pa_append_batch(pa_pool* pool, int32_t* tables, int32_t maxb, const int32_t* n_before,
+                          int32_t S, int64_t* slots, int32_t* cow_pairs, int32_t* n_pairs,
+                          int32_t* n_done) {
+  pa_detail::clear_error();
+  if (n_pairs) *n_pairs = 0;
+  if (n_done) *n_done = 0;
+  if (pa_status st = check_pool(pool)) return st;
+  if (S < 0 || maxb <= 0) return fail(PA_ERR_INVALID_ARG, "bad S or maxb");
+  if (S > 0 && (!tables || !n_before || !slots)) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  int32_t pairs = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    int32_t src, dst;
+    pa_status st = do_append(pool, tables + (size_t)s * maxb, maxb, n_before[s], &slots[s], &src, &dst);
+    if (st != PA_OK) {
+      if (n_done) *n_done = s;
+      if (n_pairs) *n_pairs = pairs;
+      return st;
+    }
+    if (src >= 0) {
+      if (cow_pairs) {
+        cow_pairs[2 * pairs] = src;
+        cow_pairs[2 * pairs + 1] = dst;
+      }
+      pairs += 1;
+    }
+  }
+  if (n_done) *n_done = S;
+  if (n_pairs) *n_pairs = pairs;
+  return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_pool* pool, const int32_t* parent_table, int32_t n_tokens,
+                      int32_t* child_table, int32_t maxb) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (n_tokens < 0 || maxb < 0) return fail(PA_ERR_INVALID_ARG, "bad n_tokens or maxb");
+  const int32_t nb = (int32_t)(((int64_t)n_tokens + pool->B - 1) / pool->B);
+  if (nb > maxb) return fail(PA_ERR_INVALID_ARG, "table too short for the forked length");
+  if (nb > 0 && (!parent_table || !child_table)) return fail(PA_ERR_INVALID_ARG, "NULL table");
+  for (int32_t j = 0; j < nb; ++j) {
+    const int32_t b = parent_table[j];
+    if (!in_range(pool, b)) return fail(PA_ERR_INVALID_ARG, "parent entry outside the pool");
+    if (pool->ref[(size_t)b] == 0) return fail(PA_ERR_INVALID_ARG, "parent maps a free block");
+  }
+  for (int32_t j = 0; j < nb; ++j) {
+    const int32_t b = parent_table[j];
+    pool->ref[(size_t)b] += 1;
+    child_table[j] = b;
+  }
+  return PA_OK;
+}
+
+pa_status pa_seq_free(pa_pool* pool, const int32_t* table, int32_t n_tokens) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (n_tokens < 0) return fail(PA_ERR_INVALID_ARG, "negative length");
+  const int32_t nb = (int32_t)(((int64_t)n_tokens + pool->B - 1) / pool->B);
+  if (nb > 0 && !table) return fail(PA_ERR_INVALID_ARG, "table is NULL");
+  // validate first so that nothing changes on error (a table may repeat a block)
+  std::vector<std::pair<int32_t, int32_t>> need;  // (block, references to drop)
+  for (int32_t j = 0; j < nb; ++j) {
+    const int32_t b = table[j];
+    if (!in_range(pool, b)) return fail(PA_ERR_INVALID_ARG, "table entry outside the pool");
+    bool found = false;
+    for (auto& e : need)
+      if (e.first == b) {
+        e.second += 1;
+        found = true;
+        break;
+      }
+    if (!found) need.emplace_back(b, 1);
+  }
+  for (const auto& e : need)
+    if (pool->ref[(size_t)e.first] < e.second)
+      return fail(PA_ERR_INVALID_ARG, "block has fewer references than the table holds");
+  for (int32_t j = 0; j < nb; ++j) do_decref(pool, table[j]);
+  return PA_OK;
+}
+
+}  // extern "C"

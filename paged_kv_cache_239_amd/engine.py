@@ -1,0 +1,162 @@
+"""One decode step over a paged pool, end to end.
+
+Per step (batch of S sequences, each appending one token):
+  1. host manager (libpa): every sequence reserves the slot of its new token,
+     in batch order; writes into shared partial blocks request a
+     copy-on-write pair ("vLLM PagedAttention and continuous batching",
+     sections "PagedAttention: fixed blocks, non-contiguous physical memory"
+     and "Sharing with reference counts and copy-on-write");
+  2. upload of block tables, context lengths, slots and copy pairs (pinned
+     staging buffers, asynchronous on the stream);
+  3. pa_copy_blocks for the copy-on-write pairs, before any write;
+  4. for every layer: pa_write_kv of the new token, then pa_decode_attention.
+
+Everything in steps 1, 3 and 4 runs in the native library; this module only
+sequences the calls and moves arguments.
+"""
+
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from ._abi import check
+from .pool import Pool, _ptr, _stream_handle
+
+
+class _Staging:
+    """Ring of pinned host buffers guarded by events, so the host can run a
+    few steps ahead of the device without overwriting a buffer that an
+    earlier asynchronous copy still reads."""
+
+    def __init__(self, nbytes: int, depth: int = 3):
+        import torch
+        self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
+        self.events = [None] * depth
+        self.i = 0
+
+    def next(self):
+        j = self.i
+        self.i = (self.i + 1) % len(self.bufs)
+        if self.events[j] is not None:
+            self.events[j].synchronize()
+        return j, self.bufs[j]
+
+    def mark(self, j, stream):
+        import torch
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        self.events[j] = ev
+
+
+class DecodeEngine:
+    def __init__(self, L: int, Hq: int, Hkv: int, d: int, B: int, P: int, dtype: str, S: int, maxb: int,
+                 free_order: Optional[Sequence[int]] = None, device: str = "cuda"):
+        import torch
+        self.torch = torch
+        self.L, self.Hq, self.Hkv, self.d, self.B, self.P = L, Hq, Hkv, d, B, P
+        self.S, self.maxb = S, maxb
+        self.device = device
+        self.pool = Pool(L, Hkv, d, B, P, dtype, free_order=free_order, device=device)
+        self.tables = np.full((S, maxb), -1, dtype=np.int32)   # host block tables
+        self.lens = np.zeros(S, dtype=np.int32)                 # tokens held per sequence
+        self.d_tables = torch.zeros((S, maxb), dtype=torch.int32, device=device)
+        self.d_lens = torch.zeros(S, dtype=torch.int32, device=device)
+        self.d_slots = torch.zeros(S, dtype=torch.int64, device=device)
+        self.d_pairs = torch.zeros((S, 2), dtype=torch.int32, device=device)
+        self._stage_bytes = S * maxb * 4 + S * 4 + S * 8 + S * 8
+        self._staging = _Staging(self._stage_bytes)
+        self.ws = None
+        self.ws_bytes = 0
+        self.last_pairs = np.zeros((0, 2), dtype=np.int32)
+        self.last_slots = np.zeros(0, dtype=np.int64)
+
+    # ---- history (prefill / sharing) ----------------------------------------------
+    def append(self, s: int, ntok: int):
+        """Prefill ``ntok`` tokens onto sequence s: returns (slots, cow pairs)."""
+        slots, pairs = self.pool.append_tokens(self.tables[s], int(self.lens[s]), ntok)
+        self.lens[s] += ntok
+        return slots, pairs
+
+    def fork(self, child: int, parent: int, ntok: int) -> None:
+        self.pool.fork(self.tables[parent], ntok, self.tables[child])
+        self.lens[child] = ntok
+
+    def upload_tables(self, stream=None) -> None:
+        """Synchronous upload of the current tables and lengths."""
+        torch = self.torch
+        self.d_tables.copy_(torch.from_numpy(self.tables))
+        self.d_lens.copy_(torch.from_numpy(self.lens))
+
+    # ---- workspace ------------------------------------------------------------------
+    def ensure_workspace(self, max_ctx: int, stream=None) -> None:
+        # sized once for the longest context the tables can hold
+        need = self.pool.workspace_bytes(self.S, self.Hq, max(max_ctx, self.maxb * self.B))
+        if need > self.ws_bytes:
+            torch = self.torch
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            check(self.pool.lib, self.pool.lib.pa_decode_workspace_init(_ptr(self.ws), need,
+                                                                        _stream_handle(stream)))
+            self.ws_bytes = need
+
+    # ---- one decode step ----------------------------------------------------------------
+    def manager_step(self, stream=None) -> int:
+        """Host manager for one step plus the asynchronous upload of its
+        results.  Returns the step's max context length."""
+        torch = self.torch
+        n_before = self.lens.copy()
+        slots, pairs = self.pool.append_batch(self.tables, n_before)
+        self.lens += 1
+        self.last_slots, self.last_pairs = slots, pairs
+        S, mb = self.S, self.maxb
+        j, buf = self._staging.next()
+        o = 0
+        tb = buf[o:o + S * mb * 4]; o += S * mb * 4
+        lb = buf[o:o + S * 4]; o += S * 4
+        sb = buf[o:o + S * 8]; o += S * 8
+        pb = buf[o:o + S * 8]
+        tb.numpy().view(np.int32)[:] = self.tables.reshape(-1)
+        lb.numpy().view(np.int32)[:] = self.lens
+        sb.numpy().view(np.int64)[:] = slots
+        npairs = len(pairs)
+        if npairs:
+            pb.numpy().view(np.int32)[: 2 * npairs] = pairs.reshape(-1)
+        st = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(st):
+            self.d_tables.view(-1).view(torch.uint8).copy_(tb, non_blocking=True)
+            self.d_lens.view(torch.uint8).copy_(lb, non_blocking=True)
+            self.d_slots.view(torch.uint8).copy_(sb, non_blocking=True)
+            if npairs:
+                self.d_pairs[:npairs].view(-1).view(torch.uint8).copy_(pb[: 8 * npairs], non_blocking=True)
+        self._staging.mark(j, st)
+        return int(self.lens.max())
+
+    def device_step(self, qs: List, knews: List, vnews: List, outs: List, max_ctx: int, scale: float,
+                    stream=None, layers: Optional[Sequence[int]] = None, attn_events=None) -> None:
+        """Copies for this step's copy-on-write pairs, then per layer the
+        new token's write and the attention.  qs/knews/vnews/outs are indexed
+        by layer.  ``attn_events``, if given, is a list that receives one
+        (start, end) pair of recorded events around every attention launch."""
+        npairs = len(self.last_pairs)
+        if npairs:
+            self.pool.copy_blocks(self.d_pairs[:npairs], stream=stream)
+        self.ensure_workspace(max_ctx, stream)
+        torch = self.torch
+        st = None
+        if attn_events is not None:
+            st = torch.cuda.current_stream() if stream is None else stream
+        for layer in (range(self.L) if layers is None else layers):
+            self.pool.write_kv(layer, knews[layer], vnews[layer], self.d_slots, stream=stream)
+            if st is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+            self.pool.decode_attention(layer, outs[layer], qs[layer], self.d_tables, self.d_lens, max_ctx,
+                                       scale, workspace=self.ws, stream=stream)
+            if st is not None:
+                e1.record(st)
+                attn_events.append((e0, e1))
+
+    def step(self, qs, knews, vnews, outs, scale: float, stream=None) -> None:
+        max_ctx = self.manager_step(stream)
+        self.device_step(qs, knews, vnews, outs, max_ctx, scale, stream)

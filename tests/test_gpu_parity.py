@@ -1,0 +1,376 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Integer and byte work (slot scatter, block copies, tables, refcounts,
+copy-on-write pairs) must be bit-exact; attention must be within max-abs
+2e-3 and max-rel 1e-2 (relative error over |ref| >= 0.2) of the oracle."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle.attention import dense_attention
+from oracle.cache_ops import HostPool, copy_blocks, gather, write_kv
+from oracle.decode import decode_layer
+from oracle.dtypes import bits_to_f64
+from oracle.replay import build_state, decode_step
+from tests.harness import (OracleSide, fill_pool_nan, fill_pool_random, layer_inputs, make_engine,
+                           replay_history_device, snapshot_layers, to_device_bits, to_host_bits,
+                           to_host_f64, tol_stats, within_tolerance)
+from workloads import make_workload, normal_bits, round_to_dtype_bits
+from workloads.gen import dtype_nan_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_required():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _pool(L, Hkv, B, P, dtype, order=None):
+    from paged_kv_cache_239_amd import Pool
+    return Pool(L, Hkv, 128, B, P, dtype, free_order=order)
+
+
+# --------------------------------------------------------------------------------
+# write_kv and copy_blocks: bit-exact
+# --------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,B,Hkv", [("f16", 16, 2), ("bf16", 32, 8), ("f16", 16, 40)])
+def test_write_kv_bit_exact(dtype, B, Hkv):
+    _say(f"write_kv {dtype} B={B} Hkv={Hkv}")
+    rng = np.random.default_rng(1)
+    L, P, S = 3, 24, 37
+    pool = _pool(L, Hkv, B, P, dtype)
+    init = rng.integers(0, 2 ** 16, size=pool.nbytes // 2, dtype=np.uint16)
+    pool.buffer.view(torch.int16).copy_(torch.from_numpy(init.view(np.int16)))
+    host = HostPool.from_arrays(init.reshape(L, 2, P, Hkv, B, 128)[:, 0].copy(),
+                                init.reshape(L, 2, P, Hkv, B, 128)[:, 1].copy())
+    slots = rng.choice(P * B, size=S, replace=False).astype(np.int64)
+    slots[[3, 10]] = -1                         # skipped tokens
+    slots[5] = P * B + 7                        # beyond the pool: ignored
+    k = normal_bits(rng, (S, Hkv, 128), dtype)
+    v = normal_bits(rng, (S, Hkv, 128), dtype)
+    layer = 1
+    pool.write_kv(layer, to_device_bits(k, dtype), to_device_bits(v, dtype), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    oslots = [int(x) if x < P * B else -1 for x in slots]
+    write_kv(host, layer, k, v, oslots)
+    for l in range(L):
+        assert np.array_equal(to_host_bits(pool.slab(l, "k")), host.K[l])
+        assert np.array_equal(to_host_bits(pool.slab(l, "v")), host.V[l])
+
+
+@pytest.mark.parametrize("dtype,B,Hkv,L", [("f16", 32, 2, 1), ("f16", 16, 40, 3), ("bf16", 16, 8, 2)])
+def test_copy_blocks_bit_exact(dtype, B, Hkv, L):
+    _say(f"copy_blocks {dtype} B={B} Hkv={Hkv} L={L}")
+    rng = np.random.default_rng(2)
+    P = 20
+    pool = _pool(L, Hkv, B, P, dtype)
+    init = rng.integers(0, 2 ** 16, size=pool.nbytes // 2, dtype=np.uint16)
+    pool.buffer.view(torch.int16).copy_(torch.from_numpy(init.view(np.int16)))
+    host = HostPool.from_arrays(init.reshape(L, 2, P, Hkv, B, 128)[:, 0].copy(),
+                                init.reshape(L, 2, P, Hkv, B, 128)[:, 1].copy())
+    pairs = np.array([[3, 11], [0, 19], [7, 2], [5, 5], [4, 25]], dtype=np.int32)
+    pool.copy_blocks(torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    copy_blocks(host, [(3, 11), (0, 19), (7, 2)])   # src == dst and out-of-range pairs are skipped
+    for l in range(L):
+        assert np.array_equal(to_host_bits(pool.slab(l, "k")), host.K[l])
+        assert np.array_equal(to_host_bits(pool.slab(l, "v")), host.V[l])
+
+
+# --------------------------------------------------------------------------------
+# decode attention on the small workloads: full step vs oracle
+# --------------------------------------------------------------------------------
+def _small_workload_step(cfg, steps=1):
+    wl = make_workload(cfg)
+    c = wl.cfg
+    eng = make_engine(wl, steps=steps)
+    fill_pool_nan(eng, c.dtype)                 # unwritten slots hold NaN
+    replay_history_device(eng, wl, write_values=True)
+    st = build_state(wl, layers=tuple(range(c.L)), maxb=wl.max_blocks(steps), fill_bits=dtype_nan_bits(c.dtype))
+    results = []
+    for step in range(steps):
+        qs, ks, vs = layer_inputs(wl, range(c.L), step)
+        outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+        max_ctx = eng.manager_step()
+        eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
+        torch.cuda.synchronize()
+        ref, slots, pairs = decode_step(st, wl, step)
+        assert list(eng.last_slots) == slots
+        assert [tuple(p) for p in eng.last_pairs.tolist()] == pairs
+        got = np.stack([to_host_f64(outs[l], c.dtype) for l in range(c.L)])
+        results.append((got, ref, pairs))
+    return wl, eng, st, results
+
+
+def test_config1_five_lengths_gqa4_b16():
+    _say("config 1")
+    wl, eng, st, res = _small_workload_step(1)
+    got, ref, pairs = res[0]
+    ok, stats = within_tolerance(got, ref)
+    _say(f"config 1 stats {stats}")
+    assert ok, stats
+    assert pairs == []
+    # paged tables as the worked example: 62 blocks, the first 62 of the permutation
+    assert eng.pool.stats()["allocs"] == 62
+
+
+def test_config2_prefix_sharing_cow():
+    _say("config 2")
+    wl, eng, st, res = _small_workload_step(2, steps=2)
+    for got, ref, pairs in res:
+        ok, stats = within_tolerance(got, ref)
+        _say(f"config 2 stats {stats}")
+        assert ok, stats
+    assert len(res[0][2]) == 1 and res[1][2] == []
+    # device pool equals the oracle pool byte for byte (copy + writes), both layers' K and V
+    assert np.array_equal(to_host_bits(eng.pool.slab(0, "k")), st.pool.K[0])
+    assert np.array_equal(to_host_bits(eng.pool.slab(0, "v")), st.pool.V[0])
+    # refcounts and free list match
+    assert eng.pool.refcounts() == st.mgr.ref
+    assert eng.pool.free_list() == st.mgr.free_list()
+
+
+def test_config2_isolation_sharers_unchanged():
+    """Sequences 2-4 produce the same output whether or not sequence 1's
+    copy-on-write write happened in the same step."""
+    _say("config 2 isolation")
+    wl = make_workload(2)
+    c = wl.cfg
+    eng = make_engine(wl)
+    fill_pool_nan(eng, c.dtype)
+    replay_history_device(eng, wl, write_values=True)
+    p1 = int(eng.tables[1][1])
+    before = to_host_bits(eng.pool.slab(0, "k"))[p1].copy()
+    qs, ks, vs = layer_inputs(wl, [0], 0)
+    out = {0: torch.empty_like(qs[0])}
+    max_ctx = eng.manager_step()
+    eng.device_step(qs, ks, vs, out, max_ctx, float(wl.scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(eng.pool.slab(0, "k"))[p1], before)
+    got = to_host_f64(out[0], c.dtype)
+    # recompute sharers alone (the oracle without sequence 0's step)
+    st = build_state(wl, layers=(0,), fill_bits=dtype_nan_bits(c.dtype))
+    lens = [n + 1 for n in st.lens]
+    from oracle.manager import BlockManager
+    for s in (1, 2, 3):
+        t = list(st.tables[s])
+        st.mgr.append_slot(t, st.lens[s])
+        slot = t[(lens[s] - 1) // c.B] * c.B + (lens[s] - 1) % c.B
+        write_kv(st.pool, 0, wl.knew_bits(0)[s:s + 1], wl.vnew_bits(0)[s:s + 1], [slot])
+        ref = decode_layer(st.pool, 0, wl.q_bits(0)[s:s + 1], [t], [lens[s]], float(wl.scale), c.dtype)[0]
+        ok, stats = within_tolerance(got[s], ref)
+        assert ok, (s, stats)
+
+
+# --------------------------------------------------------------------------------
+# decode attention over shapes, lengths and dtypes
+# --------------------------------------------------------------------------------
+def _direct_case(rng, S, Hq, Hkv, B, dtype, lens, P=None, poison=True, q_scale=1.0, order=None):
+    """Pool filled with random values (NaN outside live slots), random tables."""
+    maxb = max(1, max(-(-n // B) for n in lens))
+    need = sum(-(-n // B) for n in lens)
+    P = P or need + 3
+    pool = _pool(1, Hkv, B, P, dtype, order)
+    shape = (1, P, Hkv, B, 128)
+    K = normal_bits(rng, shape, dtype)
+    V = normal_bits(rng, shape, dtype)
+    perm = rng.permutation(P)
+    tables = np.full((S, maxb), -1, dtype=np.int32)
+    o = 0
+    live = np.zeros((P, B), dtype=bool)
+    for s, n in enumerate(lens):
+        nb = -(-n // B)
+        tables[s, :nb] = perm[o:o + nb]
+        o += nb
+        for t in range(n):
+            live[tables[s, t // B], t % B] = True
+    if poison:
+        nan = dtype_nan_bits(dtype)
+        dead = np.broadcast_to(~live[:, None, :], (P, Hkv, B))
+        K[0][dead] = nan
+        V[0][dead] = nan
+        tables[tables < 0] = 10 ** 6            # padding entries: out of range, never read
+    pool.slab(0, "k").view(torch.int16).copy_(torch.from_numpy(K[0].view(np.int16)))
+    pool.slab(0, "v").view(torch.int16).copy_(torch.from_numpy(V[0].view(np.int16)))
+    q = round_to_dtype_bits(rng.standard_normal((S, Hq, 128)).astype(np.float32) * q_scale, dtype)
+    host = HostPool.from_arrays(K, V)
+    return pool, host, tables, q
+
+
+def _run_direct(pool, tables, q, lens, dtype, scale, max_ctx=None):
+    from paged_kv_cache_239_amd import decode_workspace
+    S, Hq = q.shape[0], q.shape[1]
+    max_ctx = max(lens) if max_ctx is None else max_ctx
+    ws = decode_workspace(pool, S, Hq, max_ctx)
+    dq = to_device_bits(q, dtype)
+    out = torch.empty_like(dq)
+    pool.decode_attention(0, out, dq, torch.from_numpy(tables).cuda(),
+                          torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(), max_ctx, scale, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+SHAPES = [
+    # (G, Hkv, B, dtype)
+    (1, 4, 16, "f16"), (2, 2, 16, "bf16"), (4, 2, 16, "f16"), (8, 1, 16, "bf16"),
+    (1, 2, 32, "bf16"), (2, 4, 32, "f16"), (4, 8, 32, "bf16"), (8, 2, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("G,Hkv,B,dtype", SHAPES)
+def test_decode_shapes_ragged_lengths(G, Hkv, B, dtype):
+    _say(f"shape G={G} Hkv={Hkv} B={B} {dtype}")
+    rng = np.random.default_rng(10 * G + B)
+    lens = [1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 511, 1000, 1537, 2048, 3001]
+    if B == 32:
+        lens = lens + [32, 63, 4096]
+    S = len(lens)
+    Hq = G * Hkv
+    pool, host, tables, q = _direct_case(rng, S, Hq, Hkv, B, dtype, lens)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    out = _run_direct(pool, tables, q, lens, dtype, scale)
+    got = to_host_f64(out, dtype)
+    ref = decode_layer(host, 0, q, tables, lens, scale, dtype)
+    ok, stats = within_tolerance(got, ref)
+    _say(f"stats {stats}")
+    assert ok, stats
+
+
+def test_decode_zero_length_gives_zero_and_single_token_gives_value():
+    _say("edge lengths")
+    rng = np.random.default_rng(3)
+    lens = [0, 1, 0, 5]
+    pool, host, tables, q = _direct_case(rng, 4, 8, 2, 16, "f16", [max(n, 1) for n in lens])
+    out = _run_direct(pool, tables, q, lens, "f16", 0.1)
+    got = to_host_f64(out, "f16")
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    # one token: output is that token's value, exactly (rounded back to fp16)
+    v0 = bits_to_f64(host.V[0, tables[1, 0], :, 0, :], "f16")       # [Hkv][d]
+    assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
+    ref = decode_layer(host, 0, q[3:4], tables[3:4], [5], 0.1, "f16")
+    assert within_tolerance(got[3], ref[0])[0]
+
+
+@pytest.mark.parametrize("mag", [30.0, 300.0])
+def test_decode_extreme_logits(mag):
+    """Scores of order +-1e3 .. 1e4 must neither overflow nor lose the maximum."""
+    _say(f"extreme logits {mag}")
+    rng = np.random.default_rng(4)
+    lens = [700, 2000, 64]
+    pool, host, tables, q = _direct_case(rng, 3, 8, 2, 16, "f16", lens, q_scale=mag)
+    scale = 1.0
+    out = _run_direct(pool, tables, q, lens, "f16", scale)
+    got = to_host_f64(out, "f16")
+    ref = decode_layer(host, 0, q, tables, lens, scale, "f16")
+    assert np.all(np.isfinite(got))
+    ok, st = within_tolerance(got, ref)
+    _say(f"stats {st}")
+    assert ok and st["allclose_worst"] <= 0, st
+
+
+def test_decode_bitwise_invariant_under_block_permutation_and_reruns():
+    _say("permutation invariance")
+    rng = np.random.default_rng(5)
+    lens = [300, 1234, 77, 2500]
+    dtype = "bf16"
+    pool, host, tables, q = _direct_case(rng, 4, 16, 4, 16, dtype, lens, poison=False)
+    scale = 0.0883883
+    out1 = _run_direct(pool, tables, q, lens, dtype, scale)
+    out2 = _run_direct(pool, tables, q, lens, dtype, scale)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    # move every physical block b to perm[b] and rewrite the tables
+    P = host.P
+    perm = rng.permutation(P)
+    K2 = np.empty_like(host.K)
+    V2 = np.empty_like(host.V)
+    K2[:, perm] = host.K
+    V2[:, perm] = host.V
+    pool.slab(0, "k").view(torch.int16).copy_(torch.from_numpy(K2[0].view(np.int16)))
+    pool.slab(0, "v").view(torch.int16).copy_(torch.from_numpy(V2[0].view(np.int16)))
+    t2 = np.where(tables >= 0, perm[np.clip(tables, 0, P - 1)], tables).astype(np.int32)
+    out3 = _run_direct(pool, t2, q, lens, dtype, scale)
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+
+
+def test_decode_matches_contiguous_baseline():
+    """Paged result vs the oracle's dense attention on contiguous K/V."""
+    _say("contiguous baseline")
+    rng = np.random.default_rng(6)
+    lens = [513, 100]
+    pool, host, tables, q = _direct_case(rng, 2, 4, 1, 16, "f16", lens)
+    out = _run_direct(pool, tables, q, lens, "f16", 0.125)
+    got = to_host_f64(out, "f16")
+    for s, n in enumerate(lens):
+        Kc, Vc = gather(host, 0, tables[s], n)
+        dense = dense_attention(bits_to_f64(q[s], "f16"), bits_to_f64(Kc, "f16"), bits_to_f64(Vc, "f16"), 0.125)
+        assert within_tolerance(got[s], dense)[0]
+
+
+# --------------------------------------------------------------------------------
+# full-size workloads: sampled outputs, in the bench's launch configuration
+# --------------------------------------------------------------------------------
+def _full_size(cfg, steps, layers, seqs_per_layer, seed):
+    wl = make_workload(cfg)
+    c = wl.cfg
+    eng = make_engine(wl, steps=steps)
+    _say(f"config {cfg}: pool {eng.pool.nbytes / 2**30:.1f} GiB, P={wl.P}, S={wl.S}")
+    fill_pool_random(eng, wl)
+    replay_history_device(eng, wl, write_values=False)
+    snaps = snapshot_layers(eng, layers)
+    ora = OracleSide(wl, snaps, wl.max_blocks(steps))
+    assert list(eng.lens) == ora.state.lens
+    rng = np.random.default_rng(seed)
+    worst = {}
+    for step in range(steps):
+        qs, ks, vs = layer_inputs(wl, range(c.L), step)
+        outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+        max_ctx = eng.manager_step()
+        eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
+        torch.cuda.synchronize()
+        slots, pairs, lens = ora.step(step)
+        assert list(eng.last_slots) == slots
+        assert [tuple(p) for p in eng.last_pairs.tolist()] == pairs
+        assert list(eng.lens) == lens
+        for layer in layers:
+            got_all = to_host_f64(outs[layer], c.dtype)
+            pick = rng.choice(wl.S, size=min(seqs_per_layer, wl.S), replace=False)
+            pick = sorted(set(pick.tolist()) | {int(np.argmax(lens)), int(np.argmin(lens))})
+            for s in pick:
+                ref = ora.expected(layer, s, step)
+                ok, stats = within_tolerance(got_all[s], ref)
+                assert ok, (cfg, step, layer, s, stats)
+                worst[(step, layer, s)] = stats["max_abs"]
+        _say(f"config {cfg} step {step}: pairs={len(pairs)} worst max_abs {max(worst.values()):.2e}")
+    # the oracle-side pools saw the same copies and writes: compare sampled layers byte for byte
+    for layer in layers:
+        assert np.array_equal(to_host_bits(eng.pool.slab(layer, "k")), ora.pools[layer].K[0])
+        assert np.array_equal(to_host_bits(eng.pool.slab(layer, "v")), ora.pools[layer].V[0])
+    assert eng.pool.refcounts() == ora.state.mgr.ref
+    del eng
+    torch.cuda.empty_cache()
+
+
+def test_config3_full_size_sampled():
+    _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=6, seed=30)
+
+
+def test_config4_full_size_sampled():
+    _full_size(4, steps=1, layers=[0, 17], seqs_per_layer=3, seed=40)
+
+
+def test_config5_full_size_sampled():
+    _full_size(5, steps=2, layers=[0, 39], seqs_per_layer=6, seed=50)
