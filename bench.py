@@ -58,6 +58,50 @@ def recorded_traffic():
     return rec
 
 
+class HipEvents:
+    """Timing-only HIP events (hipEventDisableSystemFence): recording them adds
+    no cache write-back between the kernels they bracket.  torch's events use
+    the default flags, whose system-scope fence costs several microseconds
+    per record on this GPU."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.C = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        e = self.C.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.C.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream_handle):
+        rc = self.hip.hipEventRecord(e, self.C.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.C.c_float()
+        rc = self.hip.hipEventElapsedTime(self.C.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def attn_bytes(lens, S, Hq, Hkv, d, B, b=2) -> int:
     """Algorithmic bytes of one layer's decode attention."""
     lens = np.asarray(lens, dtype=np.int64)
@@ -74,7 +118,7 @@ def write_bytes(S, Hkv, d, b=2) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload id (3 = the GQA 32/8 workload)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
@@ -153,36 +197,57 @@ def main() -> int:
         eng.device_step(qs, ks, vs, outs, max_ctx, scale)
     torch.cuda.synchronize()
 
-    step_events, attn_events = [], []
+    # every timing event exists (and has been recorded once) before the timed region starts
+    hev = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+
+    class _Ev:
+        def __init__(self):
+            self.e = hev.create()
+            hev.record(self.e, sh)
+
+        def record(self, stream=None):
+            hev.record(self.e, sh if stream is None else stream.cuda_stream)
+
+    step_events = [(_Ev(), _Ev()) for _ in range(K)]
+    # one attention call per step is bracketed (a different layer each step):
+    # an event record between two kernels costs a few microseconds, so
+    # bracketing every call would slow the very step being measured
+    attn_pool = [{(7 * i) % c.L: (_Ev(), _Ev())} for i in range(K)]
+    ev0, ev1 = _Ev(), _Ev()
+    torch.cuda.synchronize()
+    attn_events = []
     alg_bytes = 0
     attn_alg = []
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    import gc
+    gc.collect()
+    gc.disable()          # no collector pauses inside the timed region
     wall0 = time.perf_counter()
     ev0.record()
     issue_ms = []
-    for _ in range(K):
-        es = torch.cuda.Event(enable_timing=True)
-        ee = torch.cuda.Event(enable_timing=True)
+    for i in range(K):
+        es, ee = step_events[i]
         h0 = time.perf_counter()
         es.record()
         max_ctx = eng.manager_step()
-        eng.device_step(qs, ks, vs, outs, max_ctx, scale, attn_events=attn_events)
+        eng.device_step(qs, ks, vs, outs, max_ctx, scale, attn_events=attn_events,
+                        event_pool=attn_pool[i])
         ee.record()
         issue_ms.append((time.perf_counter() - h0) * 1e3)
-        step_events.append((es, ee))
         ab = attn_bytes(eng.lens, wl.S, c.Hq, c.Hkv, c.d, c.B)
-        attn_alg.extend([ab] * c.L)
+        attn_alg.append(ab)
         alg_bytes += c.L * (ab + write_bytes(wl.S, c.Hkv, c.d))
         alg_bytes += len(eng.last_pairs) * c.L * 2 * eng.pool.nbytes // (2 * c.L * wl.P) * 2
     ev1.record()
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
+    gc.enable()
 
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = hev.elapsed_ms(ev0.e, ev1.e)
     ms_per_step = total_ms / K
-    step_ms = np.array([a.elapsed_time(b) for a, b in step_events])
-    attn_ms = np.array([a.elapsed_time(b) for a, b in attn_events])
+    step_ms = np.array([hev.elapsed_ms(a.e, b.e) for a, b in step_events])
+    attn_ms = np.array([hev.elapsed_ms(a.e, b.e) for a, b in attn_events])
+    hev.close()
     mean_attn_bytes = float(np.mean(attn_alg))
     attn_avg_us = float(np.mean(attn_ms)) * 1e3
     achieved = mean_attn_bytes / (attn_avg_us * 1e-6) / 1e9
@@ -217,6 +282,7 @@ def main() -> int:
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "wall_ms_per_step": round((wall1 - wall0) * 1e3 / K, 4),
         "attn_launch_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "attn_launches_timed": int(len(attn_ms)),
         "roofline": {
             "kernel": "decode_attention_kernel<bf16,G=4,B=16>",
             "bound": "hbm",
@@ -241,7 +307,8 @@ def main() -> int:
     result["host_issue_ms_per_step_p50"] = round(float(np.median(issue_ms)), 4)
     if args.dump:
         with open(args.dump, "w") as f:
-            json.dump({"step_ms": step_ms.tolist(), "attn_us": (attn_ms * 1e3).tolist(), "issue_ms": issue_ms}, f)
+            json.dump({"step_ms": step_ms.tolist(), "attn_us": (attn_ms * 1e3).tolist(), "issue_ms": issue_ms,
+                       "attn_layers": [next(iter(d)) for d in attn_pool]}, f)
     if args.cpu_baseline == "on":
         result["cpu_baseline"], result["parity"] = cpu_baseline(wl, eng, snaps, outs, W + K, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -240,6 +240,24 @@ pa_status pa_decode_attention(pa_pool* pool, int layer, void* out,
                               float scale, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* pa_write_kv followed by pa_decode_attention for the same layer, in one
+ * pass ("fused block operations" of the reading guide's main concepts):
+ * the result -- the cache contents and `out` -- equals the two calls in that
+ * order when every slot_mapping[s] >= 0 is the slot that position
+ * context_lens[s] - 1 of sequence s maps to through block_tables[s] (the
+ * decode step's own token) or is negative.  The token's key and value are
+ * then taken from k / v directly for that position.  Arguments as for the
+ * two separate calls (k, v: device [S][Hkv][d]; slot_mapping: device int64
+ * [S]); same errors. */
+pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k,
+                                       const void* v,
+                                       const int64_t* slot_mapping, void* out,
+                                       const void* q, int S, int Hq,
+                                       const int32_t* block_tables, int maxb,
+                                       const int32_t* context_lens, int max_ctx,
+                                       float scale, void* workspace,
+                                       size_t ws_bytes, hipStream_t stream);
+
 /* Message describing the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);
 

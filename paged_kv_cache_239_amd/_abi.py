@@ -90,6 +90,8 @@ DEVICE_SIGNATURES = {
     "pa_decode_workspace_init": (C.c_int, [P, C.c_size_t, P]),
     "pa_decode_attention": (C.c_int, [P, C.c_int, P, P, C.c_int, C.c_int, P, C.c_int, P, C.c_int,
                                       C.c_float, P, C.c_size_t, P]),
+    "pa_write_kv_decode_attention": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P,
+                                               C.c_int, C.c_float, P, C.c_size_t, P]),
 }
 
 _libs = {}

@@ -240,6 +240,10 @@ struct DecodeArgs {
   const int32_t* lens;      // [S]
   float* ws_ml;             // [S][Hkv][nparts_max][G][2]  (max, normaliser)
   float* ws_acc;            // [S][Hkv][nparts_max][G][d]
+  const uint4* knew;        // [S][Hkv][d] this step's keys (fused cache write) or null
+  const uint4* vnew;        // [S][Hkv][d] this step's values, or null
+  const int64_t* slots;     // [S] their slots, or null
+  int64_t nslots;           // P * B
   int S, Hq, Hkv, P, maxb, max_ctx, part_tokens, nparts_max;
   int grid_order;           // see decode_attention_kernel
   int pstride;              // partitions per (sequence, head) in grid order 1
@@ -284,12 +288,26 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   const int r = lane >> 4;   // row: token offset inside a 4-token load
   const int c = lane & 15;   // 16-byte chunk: dims 8c..8c+7
 
+  // Requests that do not depend on the context length go out first: the
+  // query group and this lane's block-table entry (index clamped into the
+  // table row; an entry past the sequence is never used).
+  const int t_begin = p * a.part_tokens;
+  const int g_first = t_begin / 16 + wave;
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
+  int entry;
+  {
+    const int idx = ((g_first + lane * NW) * 16) / BS;
+    entry = table[idx < a.maxb ? idx : a.maxb - 1];
+  }
+
   int n = a.lens[s];
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
   n = __builtin_amdgcn_readfirstlane(n);
   const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
   if (p >= nparts) return;
-  const int t_begin = p * a.part_tokens;
   const int t_end = min(n, t_begin + a.part_tokens);
 
   __shared__ uint4 s_q[G * 16];
@@ -299,7 +317,6 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
 
-  const int32_t* table = a.tables + (size_t)s * a.maxb;
   const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
   const uint32_t lane_off = (uint32_t)(r * kRowBytes + c * 16);
 
@@ -319,25 +336,44 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   }
 
   // groups of 16 tokens in this partition, dealt round-robin to the waves:
-  // the k-th group of this wave is g_first + k * NW.  Lane k holds that
-  // group's physical block (read once here; a lane read per group later).
-  const int g_first = t_begin / 16 + wave;
+  // the k-th group of this wave is g_first + k * NW, and lane k holds that
+  // group's physical block (one lane read per group later).
   const int g_full = t_end / 16;               // groups [.., g_full) are full
   const int g_last = (t_end + 15) / 16;        // a tail group exists if g_full < g_last
-
-  // The query group (G heads x 256 bytes) and the block-table entries are
-  // requested together; the query is staged through LDS only after the
-  // first key/value loads are in flight.
-  const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
-  uint4 qv = make_uint4(0, 0, 0, 0);
-  if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
   uint4 qr[G];
   int my_phys = 0;
-  {
-    const int g = g_first + lane * NW;
-    if (g < g_last) {
-      const int e = table[(g * 16) / BS];
-      my_phys = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+  if (g_first + lane * NW < g_last) my_phys = entry < 0 ? 0 : (entry >= a.P ? a.P - 1 : entry);
+
+  // Fused cache write of this step's token: the workgroup of the sequence's
+  // last partition stores k_new / v_new of its head into the token's slot,
+  // and when that slot is the one position n-1 maps to, uses them directly
+  // from registers for that position (the cache load of the slot is
+  // replaced), so no other workgroup depends on the store.
+  int g_new = -1, j_new = 0, r_new = 0;
+  uint4 k_reg = make_uint4(0, 0, 0, 0), v_reg = make_uint4(0, 0, 0, 0);
+  if (a.slots != nullptr && p == nparts - 1) {
+    const int64_t slot = a.slots[s];
+    if (slot >= 0 && slot < a.nslots) {
+      const size_t src = ((size_t)s * a.Hkv + kvh) * 16 + c;
+      k_reg = a.knew[src];
+      v_reg = a.vnew[src];
+      const int64_t blk = slot / BS;
+      const int off = (int)(slot % BS);
+      if (wave == 0 && r == 0) {
+        const uint64_t dst = (uint64_t)blk * a.tile_bytes + head_off + (uint64_t)off * kRowBytes + (uint64_t)c * 16;
+        *reinterpret_cast<uint4*>(const_cast<char*>(a.kslab) + dst) = k_reg;
+        *reinterpret_cast<uint4*>(const_cast<char*>(a.vslab) + dst) = v_reg;
+      }
+      if (n > 0) {
+        const int pos = n - 1;
+        int e = table[pos / BS];
+        e = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+        if ((int64_t)e * BS + pos % BS == slot) {
+          g_new = pos / 16;
+          j_new = (pos % 16) / 4;
+          r_new = pos % 4;
+        }
+      }
     }
   }
 
@@ -366,8 +402,22 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   };
 
   int buf = 0;
-  auto process_group = [&](int g, const uint4 (&K)[4], const uint4 (&V)[4], bool tail) {
+  auto process_group = [&](int g, const uint4 (&Kin)[4], const uint4 (&Vin)[4], bool tail) {
     const int tok0 = g * 16;
+    uint4 K[4], V[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      K[j] = Kin[j];
+      V[j] = Vin[j];
+    }
+    if (g == g_new) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == j_new && r == r_new) {
+          K[j] = k_reg;
+          V[j] = v_reg;
+        }
+    }
     // partial dot products: x[4h + j] = q_h . k(token 4j + r) over this lane's 8 dims
     float x[4 * G];
 #pragma unroll
@@ -575,30 +625,35 @@ template <bool BF16, int G>
 __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a) {
   const int kvh = blockIdx.x;
   const int s = blockIdx.y;
-  int n = a.lens[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
-  if (nparts <= 1) return;  // written directly by the partition kernel
   const int wh = threadIdx.x >> 4;
   const int wc = threadIdx.x & 15;
   const size_t pbase = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
-  // online merge over partitions, CHUNK at a time so the loads of a chunk
-  // are all in flight together
+  // Partitions are read CHUNK at a time with all loads of a chunk in flight;
+  // the first chunk is requested together with the context length (its
+  // indices are clamped into the workspace; unused entries are ignored).
   constexpr int CHUNK = 4;
-  float Mg = -INFINITY, Lg = 0.0f, Ag[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) Ag[i] = 0.0f;
-  for (int p0 = 0; p0 < nparts; p0 += CHUNK) {
-    float2 ml[CHUNK];
-    float4 x0[CHUNK], x1[CHUNK];
+  float2 ml[CHUNK];
+  float4 x0[CHUNK], x1[CHUNK];
+  auto fetch = [&](int p0) {
 #pragma unroll
     for (int k = 0; k < CHUNK; ++k) {
-      const int pp = p0 + k < nparts ? p0 + k : nparts - 1;
+      const int pp = p0 + k < a.nparts_max ? p0 + k : a.nparts_max - 1;
       ml[k] = *reinterpret_cast<const float2*>(a.ws_ml + ((pbase + pp) * G + wh) * 2);
       const float4* src = reinterpret_cast<const float4*>(a.ws_acc + ((pbase + pp) * G + wh) * kD + 8 * wc);
       x0[k] = src[0];
       x1[k] = src[1];
     }
+  };
+  fetch(0);
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
+  if (nparts <= 1) return;  // written directly by the partition kernel
+  float Mg = -INFINITY, Lg = 0.0f, Ag[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Ag[i] = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += CHUNK) {
+    if (p0 > 0) fetch(p0);
     float mc = Mg;
 #pragma unroll
     for (int k = 0; k < CHUNK; ++k)
@@ -706,7 +761,7 @@ int env_int(const char* name, int dflt) {
 // grid still has several workgroups per compute unit.
 LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
   static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
-  int gpw = 16;
+  int gpw = 12;
   if (forced > 0) {
     gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
   } else {
@@ -764,6 +819,80 @@ bool dispatch_g(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
 }
 
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+namespace {
+
+pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int S, int Hq,
+                        const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx, float scale,
+                        void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, hipStream_t stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
+  if (S == 0) return PA_OK;
+  if (Hq <= 0 || Hq % pool->Hkv) return fail(PA_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+  const int G = Hq / pool->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
+  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
+  if (pool->B != 16 && pool->B != 32) return fail(PA_ERR_UNSUPPORTED, "block size must be 16 or 32");
+  if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
+  if (maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad maxb or max_ctx");
+  if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
+
+  const LaunchCfg cfg = choose_launch(S, pool->Hkv, max_ctx);
+  const WsLayout wl = ws_layout(S, pool->Hkv, G, cfg);
+  char* ws = static_cast<char*>(workspace);
+  if (wl.total > 0) {
+    if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+    if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_workspace_bytes");
+  }
+
+  DecodeArgs args;
+  args.kslab = pool->k_slab(layer);
+  args.vslab = pool->v_slab(layer);
+  args.tile_bytes = pool->tile_bytes;
+  args.q = static_cast<const uint16_t*>(q);
+  args.out = static_cast<uint16_t*>(out);
+  args.tables = block_tables;
+  args.lens = context_lens;
+  args.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+  args.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
+  args.S = S;
+  args.Hq = Hq;
+  args.Hkv = pool->Hkv;
+  args.P = pool->P;
+  args.maxb = maxb;
+  args.max_ctx = max_ctx;
+  args.part_tokens = cfg.part_tokens;
+  args.nparts_max = cfg.nparts_max;
+  args.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  args.knew = static_cast<const uint4*>(k_new);
+  args.vnew = static_cast<const uint4*>(v_new);
+  args.slots = slot_mapping;
+  args.nslots = (int64_t)pool->P * pool->B;
+
+  static const int grid_order = env_int("PA_GRID_ORDER", 0) == 1 ? 1 : 0;
+  args.grid_order = grid_order;
+  args.pstride = cfg.nparts_max | 1;
+  const uint64_t nwg = (uint64_t)pool->Hkv * S * (grid_order == 0 ? cfg.nparts_max : args.pstride);
+  if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const dim3 grid((unsigned)nwg);
+  bool ok;
+  const bool bf16 = pool->dtype == PA_BF16;
+  if (pool->B == 16)
+    ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream);
+  else
+    ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream);
+  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+  return hip_check(hipGetLastError(), "decode attention launch");
+}
 
 }  // namespace
 
@@ -834,66 +963,23 @@ pa_status pa_decode_attention(pa_pool* pool, int layer, void* out, const void* q
                               const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx,
                               float scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
   pa_detail::clear_error();
-  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
-  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
-  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
-  if (S == 0) return PA_OK;
-  if (Hq <= 0 || Hq % pool->Hkv) return fail(PA_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
-  const int G = Hq / pool->Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
-  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
-  if (pool->B != 16 && pool->B != 32) return fail(PA_ERR_UNSUPPORTED, "block size must be 16 or 32");
-  if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
-  if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
-  if (maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad maxb or max_ctx");
-  if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
-  if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
+                       ws_bytes, nullptr, nullptr, nullptr, stream);
+}
 
-  const LaunchCfg cfg = choose_launch(S, pool->Hkv, max_ctx);
-  const WsLayout wl = ws_layout(S, pool->Hkv, G, cfg);
-  char* ws = static_cast<char*>(workspace);
-  if (wl.total > 0) {
-    if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
-    if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_workspace_bytes");
+pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, const void* v,
+                                       const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+                                       const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                       int max_ctx, float scale, void* workspace, size_t ws_bytes,
+                                       hipStream_t stream) {
+  pa_detail::clear_error();
+  if (S > 0) {
+    if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
   }
-
-  DecodeArgs args;
-  args.kslab = pool->k_slab(layer);
-  args.vslab = pool->v_slab(layer);
-  args.tile_bytes = pool->tile_bytes;
-  args.q = static_cast<const uint16_t*>(q);
-  args.out = static_cast<uint16_t*>(out);
-  args.tables = block_tables;
-  args.lens = context_lens;
-  args.ws_ml = wl.total ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
-  args.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.acc_off) : nullptr;
-  args.S = S;
-  args.Hq = Hq;
-  args.Hkv = pool->Hkv;
-  args.P = pool->P;
-  args.maxb = maxb;
-  args.max_ctx = max_ctx;
-  args.part_tokens = cfg.part_tokens;
-  args.nparts_max = cfg.nparts_max;
-  args.scale_log2 = (float)((double)scale * 1.4426950408889634);
-
-  static const int grid_order = env_int("PA_GRID_ORDER", 0) == 1 ? 1 : 0;
-  args.grid_order = grid_order;
-  args.pstride = cfg.nparts_max | 1;
-  const uint64_t nwg = (uint64_t)pool->Hkv * S * (grid_order == 0 ? cfg.nparts_max : args.pstride);
-  if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
-  const dim3 grid((unsigned)nwg);
-  bool ok;
-  const bool bf16 = pool->dtype == PA_BF16;
-  if (pool->B == 16)
-    ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream);
-  else
-    ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream);
-  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
-  return hip_check(hipGetLastError(), "decode attention launch");
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
+                       ws_bytes, k, v, slot_mapping, stream);
 }
 
 }  // extern "C"

@@ -9,7 +9,9 @@ Per step (batch of S sequences, each appending one token):
   2. upload of block tables, context lengths, slots and copy pairs (pinned
      staging buffers, asynchronous on the stream);
   3. pa_copy_blocks for the copy-on-write pairs, before any write;
-  4. for every layer: pa_write_kv of the new token, then pa_decode_attention.
+  4. for every layer: the new token's cache write and the attention, in one
+     pass (pa_write_kv_decode_attention) or as pa_write_kv then
+     pa_decode_attention.
 
 Everything in steps 1, 3 and 4 runs in the native library; this module only
 sequences the calls and moves arguments.
@@ -52,9 +54,10 @@ class _Staging:
 
 class DecodeEngine:
     def __init__(self, L: int, Hq: int, Hkv: int, d: int, B: int, P: int, dtype: str, S: int, maxb: int,
-                 free_order: Optional[Sequence[int]] = None, device: str = "cuda"):
+                 free_order: Optional[Sequence[int]] = None, device: str = "cuda", fused: bool = True):
         import torch
         self.torch = torch
+        self.fused = fused
         self.L, self.Hq, self.Hkv, self.d, self.B, self.P = L, Hq, Hkv, d, B, P
         self.S, self.maxb = S, maxb
         self.device = device
@@ -133,11 +136,14 @@ class DecodeEngine:
         return int(self.lens.max())
 
     def device_step(self, qs: List, knews: List, vnews: List, outs: List, max_ctx: int, scale: float,
-                    stream=None, layers: Optional[Sequence[int]] = None, attn_events=None) -> None:
+                    stream=None, layers: Optional[Sequence[int]] = None, attn_events=None,
+                    event_pool=None) -> None:
         """Copies for this step's copy-on-write pairs, then per layer the
         new token's write and the attention.  qs/knews/vnews/outs are indexed
         by layer.  ``attn_events``, if given, is a list that receives one
-        (start, end) pair of recorded events around every attention launch."""
+        (start, end) pair of recorded events around the attention launches of
+        the layers in ``event_pool`` (a dict layer -> (start, end) event
+        pair); without a pool every layer gets a fresh pair."""
         npairs = len(self.last_pairs)
         if npairs:
             self.pool.copy_blocks(self.d_pairs[:npairs], stream=stream)
@@ -147,13 +153,23 @@ class DecodeEngine:
         if attn_events is not None:
             st = torch.cuda.current_stream() if stream is None else stream
         for layer in (range(self.L) if layers is None else layers):
-            self.pool.write_kv(layer, knews[layer], vnews[layer], self.d_slots, stream=stream)
-            if st is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if not self.fused:
+                self.pool.write_kv(layer, knews[layer], vnews[layer], self.d_slots, stream=stream)
+            timed = st is not None and (event_pool is None or layer in event_pool)
+            if timed:
+                if event_pool is not None:
+                    e0, e1 = event_pool[layer]
+                else:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(st)
-            self.pool.decode_attention(layer, outs[layer], qs[layer], self.d_tables, self.d_lens, max_ctx,
-                                       scale, workspace=self.ws, stream=stream)
-            if st is not None:
+            if self.fused:
+                self.pool.write_kv_decode_attention(layer, knews[layer], vnews[layer], self.d_slots, outs[layer],
+                                                    qs[layer], self.d_tables, self.d_lens, max_ctx, scale,
+                                                    workspace=self.ws, stream=stream)
+            else:
+                self.pool.decode_attention(layer, outs[layer], qs[layer], self.d_tables, self.d_lens, max_ctx,
+                                           scale, workspace=self.ws, stream=stream)
+            if timed:
                 e1.record(st)
                 attn_events.append((e0, e1))
 

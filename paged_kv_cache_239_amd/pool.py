@@ -215,6 +215,18 @@ class Pool:
             int(max_ctx), C.c_float(scale), C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes),
             _stream_handle(stream)))
 
+    def write_kv_decode_attention(self, layer: int, k, v, slot_mapping, out, q, block_tables, context_lens,
+                                  max_ctx: int, scale: float, workspace=None, stream=None) -> None:
+        """write_kv then decode_attention for one layer in one pass (see
+        pa_write_kv_decode_attention)."""
+        S, Hq = int(q.shape[0]), int(q.shape[1])
+        maxb = int(block_tables.shape[1])
+        ws_ptr, ws_bytes = (0, 0) if workspace is None else (_ptr(workspace), int(workspace.numel()))
+        check(self.lib, self.lib.pa_write_kv_decode_attention(
+            self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(out), _ptr(q), S, Hq,
+            _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), C.c_float(scale),
+            C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
+
 
 def decode_workspace(pool: Pool, S: int, Hq: int, max_ctx: int, device="cuda", stream=None):
     """A zero-initialised workspace for ``pool.decode_attention`` at these

@@ -94,10 +94,10 @@ def test_copy_blocks_bit_exact(dtype, B, Hkv, L):
 # --------------------------------------------------------------------------------
 # decode attention on the small workloads: full step vs oracle
 # --------------------------------------------------------------------------------
-def _small_workload_step(cfg, steps=1):
+def _small_workload_step(cfg, steps=1, fused=True):
     wl = make_workload(cfg)
     c = wl.cfg
-    eng = make_engine(wl, steps=steps)
+    eng = make_engine(wl, steps=steps, fused=fused)
     fill_pool_nan(eng, c.dtype)                 # unwritten slots hold NaN
     replay_history_device(eng, wl, write_values=True)
     st = build_state(wl, layers=tuple(range(c.L)), maxb=wl.max_blocks(steps), fill_bits=dtype_nan_bits(c.dtype))
@@ -116,9 +116,10 @@ def _small_workload_step(cfg, steps=1):
     return wl, eng, st, results
 
 
-def test_config1_five_lengths_gqa4_b16():
-    _say("config 1")
-    wl, eng, st, res = _small_workload_step(1)
+@pytest.mark.parametrize("fused", [True, False])
+def test_config1_five_lengths_gqa4_b16(fused):
+    _say(f"config 1 fused={fused}")
+    wl, eng, st, res = _small_workload_step(1, fused=fused)
     got, ref, pairs = res[0]
     ok, stats = within_tolerance(got, ref)
     _say(f"config 1 stats {stats}")
@@ -128,9 +129,10 @@ def test_config1_five_lengths_gqa4_b16():
     assert eng.pool.stats()["allocs"] == 62
 
 
-def test_config2_prefix_sharing_cow():
-    _say("config 2")
-    wl, eng, st, res = _small_workload_step(2, steps=2)
+@pytest.mark.parametrize("fused", [True, False])
+def test_config2_prefix_sharing_cow(fused):
+    _say(f"config 2 fused={fused}")
+    wl, eng, st, res = _small_workload_step(2, steps=2, fused=fused)
     for got, ref, pairs in res:
         ok, stats = within_tolerance(got, ref)
         _say(f"config 2 stats {stats}")
@@ -323,10 +325,10 @@ def test_decode_matches_contiguous_baseline():
 # --------------------------------------------------------------------------------
 # full-size workloads: sampled outputs, in the bench's launch configuration
 # --------------------------------------------------------------------------------
-def _full_size(cfg, steps, layers, seqs_per_layer, seed):
+def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True):
     wl = make_workload(cfg)
     c = wl.cfg
-    eng = make_engine(wl, steps=steps)
+    eng = make_engine(wl, steps=steps, fused=fused)
     _say(f"config {cfg}: pool {eng.pool.nbytes / 2**30:.1f} GiB, P={wl.P}, S={wl.S}")
     fill_pool_random(eng, wl)
     replay_history_device(eng, wl, write_values=False)
@@ -364,8 +366,9 @@ def _full_size(cfg, steps, layers, seqs_per_layer, seed):
     torch.cuda.empty_cache()
 
 
-def test_config3_full_size_sampled():
-    _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=6, seed=30)
+@pytest.mark.parametrize("fused", [True, False])
+def test_config3_full_size_sampled(fused):
+    _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=6, seed=30, fused=fused)
 
 
 def test_config4_full_size_sampled():
@@ -374,3 +377,34 @@ def test_config4_full_size_sampled():
 
 def test_config5_full_size_sampled():
     _full_size(5, steps=2, layers=[0, 39], seqs_per_layer=6, seed=50)
+
+
+@pytest.mark.parametrize("cfg,steps", [(1, 2), (2, 2), (5, 1)])
+def test_fused_write_attention_equals_separate_calls(cfg, steps):
+    """pa_write_kv_decode_attention == pa_write_kv then pa_decode_attention:
+    outputs and the whole pool byte for byte."""
+    _say(f"fused vs separate, config {cfg}")
+    wl = make_workload(cfg)
+    c = wl.cfg
+    engines = []
+    for fused in (True, False):
+        eng = make_engine(wl, steps=steps, fused=fused)
+        if cfg == 5:
+            fill_pool_random(eng, wl)
+            replay_history_device(eng, wl, write_values=False)
+        else:
+            fill_pool_nan(eng, c.dtype)
+            replay_history_device(eng, wl, write_values=True)
+        engines.append(eng)
+    for step in range(steps):
+        qs, ks, vs = layer_inputs(wl, range(c.L), step)
+        outs = []
+        for eng in engines:
+            o = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+            max_ctx = eng.manager_step()
+            eng.device_step(qs, ks, vs, o, max_ctx, float(wl.scale))
+            outs.append(o)
+        torch.cuda.synchronize()
+        for l in range(c.L):
+            assert torch.equal(outs[0][l].view(torch.int16), outs[1][l].view(torch.int16)), (cfg, step, l)
+    assert torch.equal(engines[0].pool.buffer, engines[1].pool.buffer)
