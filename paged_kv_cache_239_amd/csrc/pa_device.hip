@@ -703,31 +703,37 @@ __global__ __launch_bounds__(256) void write_kv_kernel(char* kslab, char* vslab,
 }
 
 // ---------------------------------------------------------------------------
-// copy_blocks: grid (chunk groups, 2L slabs, pairs)
+// copy_blocks: one workgroup per (pair, slab); it streams the whole tile with
+// kCopyUnroll 16-byte non-temporal loads per thread in flight
 // ---------------------------------------------------------------------------
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyUnroll = 8;
+constexpr int kCopyThreads = 256;
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* base, const int32_t* pairs, int P,
-                                                          uint64_t tile_bytes, uint64_t slab_bytes) {
-  const int pr = blockIdx.z;
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* base, const int32_t* pairs, int P,
+                                                                   uint64_t tile_bytes, uint64_t slab_bytes) {
+  const int pr = blockIdx.y;
   const int32_t src = pairs[2 * pr];
   const int32_t dst = pairs[2 * pr + 1];
   if (src < 0 || src >= P || dst < 0 || dst >= P || src == dst) return;
-  char* slab = base + (uint64_t)blockIdx.y * slab_bytes;
-  const uint4* from = reinterpret_cast<const uint4*>(slab + (uint64_t)src * tile_bytes);
-  uint4* to = reinterpret_cast<uint4*>(slab + (uint64_t)dst * tile_bytes);
+  char* slab = base + (uint64_t)blockIdx.x * slab_bytes;
+  const char* from = slab + (uint64_t)src * tile_bytes;
+  char* to = slab + (uint64_t)dst * tile_bytes;
   const uint64_t nchunks = tile_bytes / 16;
-  const uint64_t first = (uint64_t)blockIdx.x * (256 * kCopyUnroll) + threadIdx.x;
-  uint4 tmp[kCopyUnroll];
+  for (uint64_t first = threadIdx.x; first < nchunks; first += (uint64_t)kCopyThreads * kCopyUnroll) {
+    uint4 tmp[kCopyUnroll];
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const uint64_t i = first + (uint64_t)u * 256;
-    if (i < nchunks) tmp[u] = from[i];
-  }
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = first + (uint64_t)u * kCopyThreads;
+      if (i < nchunks) tmp[u] = nt_load16(from + i * 16);
+    }
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const uint64_t i = first + (uint64_t)u * 256;
-    if (i < nchunks) to[i] = tmp[u];
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = first + (uint64_t)u * kCopyThreads;
+      if (i < nchunks) {
+        const u32x4_t v = {tmp[u].x, tmp[u].y, tmp[u].z, tmp[u].w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(to + i * 16));
+      }
+    }
   }
 }
 
@@ -923,12 +929,9 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N, hipStream_t
   if (N == 0) return PA_OK;
   if (!pairs || !aligned(pairs, 4)) return fail(PA_ERR_INVALID_ARG, "pairs must be a 4-byte aligned device pointer");
   if (N > 65535) return fail(PA_ERR_INVALID_ARG, "at most 65535 pairs per call");
-  if (2 * pool->L > 65535) return fail(PA_ERR_UNSUPPORTED, "too many layers");
   if (pool->tile_bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block size in bytes must be a multiple of 16");
-  const uint64_t nchunks = pool->tile_bytes / 16;
-  const uint64_t per_wg = 256 * kCopyUnroll;
-  const dim3 grid((unsigned)((nchunks + per_wg - 1) / per_wg), (unsigned)(2 * pool->L), (unsigned)N);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, pool->base, pairs, pool->P,
+  const dim3 grid((unsigned)(2 * pool->L), (unsigned)N);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, pool->base, pairs, pool->P,
                      (uint64_t)pool->tile_bytes, (uint64_t)pool->slab_bytes);
   return hip_check(hipGetLastError(), "copy_blocks launch");
 }

@@ -137,7 +137,7 @@ class DecodeEngine:
 
     def device_step(self, qs: List, knews: List, vnews: List, outs: List, max_ctx: int, scale: float,
                     stream=None, layers: Optional[Sequence[int]] = None, attn_events=None,
-                    event_pool=None) -> None:
+                    event_pool=None, skip_copies: bool = False) -> None:
         """Copies for this step's copy-on-write pairs, then per layer the
         new token's write and the attention.  qs/knews/vnews/outs are indexed
         by layer.  ``attn_events``, if given, is a list that receives one
@@ -145,7 +145,7 @@ class DecodeEngine:
         the layers in ``event_pool`` (a dict layer -> (start, end) event
         pair); without a pool every layer gets a fresh pair."""
         npairs = len(self.last_pairs)
-        if npairs:
+        if npairs and not skip_copies:
             self.pool.copy_blocks(self.d_pairs[:npairs], stream=stream)
         self.ensure_workspace(max_ctx, stream)
         torch = self.torch

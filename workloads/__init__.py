@@ -12,6 +12,7 @@ from .configs import CONFIGS, DecodeConfig, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     Workload,
     make_workload,
+    with_headroom,
     rng_for,
     round_to_dtype_bits,
     normal_bits,

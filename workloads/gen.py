@@ -193,6 +193,27 @@ def _history(c: DecodeConfig, lengths0: np.ndarray) -> List[Tuple]:
     return ops
 
 
+def with_headroom(wl: Workload, steps: int) -> Workload:
+    """The same workload with its pool extended, if needed, so that every
+    sequence can take ``steps`` more tokens without sharing (for running many
+    decode steps over a workload whose pool is sized exactly).  Extra block
+    ids follow the original free order in a seeded shuffled order."""
+    c = wl.cfg
+    B = c.B
+    if c.pool_kind == "branch_bound":
+        shared = int(np.sum(_ceil_div(wl.lengths0[:: c.branches] - 1, B)))
+        need = shared + wl.S * (int(_ceil_div(steps, B)) + 1)
+    else:
+        need = int(np.sum(_ceil_div(wl.lengths0 - 1 + steps, B)))
+    if need <= wl.P:
+        return wl
+    extra = np.arange(wl.P, need, dtype=np.int32)
+    extra = extra[rng_for(wl.cfg.cfg_id, 0, P_PERM, 1).permutation(len(extra))]
+    return Workload(cfg=wl.cfg, lengths0=wl.lengths0, P=need,
+                    free_order=np.concatenate([wl.free_order, extra]).astype(np.int32),
+                    history=wl.history, scale=wl.scale)
+
+
 def make_workload(cfg_id: int) -> Workload:
     c = get_config(cfg_id)
     lengths0 = _lengths(c)
