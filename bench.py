@@ -133,6 +133,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload id (3 = the GQA 32/8 workload)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="store the workload in blocks of this many tokens (8, 16, 32, 64 or 128; "
+                         "default: the workload's own)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
@@ -168,7 +171,7 @@ def main() -> int:
         return 0
 
     W, K = args.warmup, args.steps
-    wl = with_headroom(make_workload(args.config), W + K + 1)
+    wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
     c = wl.cfg
     eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(W + K),
                        free_order=wl.free_order)
@@ -317,6 +320,8 @@ def main() -> int:
             "parallelism": "single GPU",
         },
         "seq_steps_per_s": round(seq_steps, 1),
+        # internal fragmentation at the last step: used slots / allocated slots
+        "slot_utilization": round(float(np.sum(eng.lens)) / float(np.sum(-(-np.asarray(eng.lens) // c.B)) * c.B), 4),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "wall_ms_per_step": round((wall1 - wall0) * 1e3 / K, 4),

@@ -227,7 +227,7 @@ pa_status pa_decode_workspace_init(void* workspace, size_t ws_bytes,
  *                   pool, S, Hq, max_ctx) bytes; may be NULL when that size
  *                   is 0.  Calls that overlap in time need separate
  *                   workspaces.
- * Supported: d = 128, B in {16, 32}, Hq / Hkv in {1, 2, 4, 8}; other shapes
+ * Supported: d = 128, B in {8, 16, 32, 64, 128}, Hq / Hkv in {1, 2, 4, 8}; other shapes
  * return UNSUPPORTED.  Device-side values are trusted for results but
  * clamped for memory safety: a table entry outside [0, P) reads block
  * min(max(entry, 0), P-1) and a length above max_ctx is cut to max_ctx.

@@ -260,7 +260,10 @@ template <bool BF16, int G, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a) {
   using SC = Scores<G>;
   constexpr int E = SC::E;
-  static_assert(BS % 16 == 0, "a 16-token step must stay inside one block");
+  // A 16-token step lies inside one block when 16 | BS; with 8-token blocks
+  // it covers two (loads 0-1 read the first, loads 2-3 the second).
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
+  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;   // blocks per 16-token step
 
   // 1-D grid; the dispatcher deals consecutive workgroups round-robin to the
   // 8 XCDs, so the order decides each XCD's share of the work.
@@ -297,10 +300,11 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
   uint4 qv = make_uint4(0, 0, 0, 0);
   if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
-  int entry;
-  {
-    const int idx = ((g_first + lane * NW) * 16) / BS;
-    entry = table[idx < a.maxb ? idx : a.maxb - 1];
+  int entry[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    const int idx = ((g_first + lane * NW) * 16) / BS + b;
+    entry[b] = table[idx < a.maxb ? idx : a.maxb - 1];
   }
 
   int n = a.lens[s];
@@ -341,14 +345,20 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   const int g_full = t_end / 16;               // groups [.., g_full) are full
   const int g_last = (t_end + 15) / 16;        // a tail group exists if g_full < g_last
   uint4 qr[G];
-  int my_phys = 0;
-  if (g_first + lane * NW < g_last) my_phys = entry < 0 ? 0 : (entry >= a.P ? a.P - 1 : entry);
+  int my_phys[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    my_phys[b] = 0;
+    if (g_first + lane * NW < g_last) my_phys[b] = entry[b] < 0 ? 0 : (entry[b] >= a.P ? a.P - 1 : entry[b]);
+  }
 
   // Fused cache write of this step's token: the workgroup of the sequence's
   // last partition stores k_new / v_new of its head into the token's slot,
   // and when that slot is the one position n-1 maps to, uses them directly
   // from registers for that position (the cache load of the slot is
-  // replaced), so no other workgroup depends on the store.
+  // replaced), so no other workgroup depends on the store.  (Reading them
+  // again at that step instead puts a load under a branch inside the loop,
+  // which coarsens every wait on the prefetched loads.)
   int g_new = -1, j_new = 0, r_new = 0;
   uint4 k_reg = make_uint4(0, 0, 0, 0), v_reg = make_uint4(0, 0, 0, 0);
   if (a.slots != nullptr && p == nparts - 1) {
@@ -380,19 +390,26 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   auto load_group = [&](int k, uint4 (&K)[4], uint4 (&V)[4], bool tail) {
     const int g = g_first + k * NW;
     const int tok0 = g * 16;
-    const int phys = __builtin_amdgcn_readlane(my_phys, k);
-    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok0 % BS) * kRowBytes;
-    const char* kb = a.kslab + off;
-    const char* vb = a.vslab + off;
+    uint64_t off[BPG];
+#pragma unroll
+    for (int b = 0; b < BPG; ++b) {
+      const int phys = __builtin_amdgcn_readlane(my_phys[b], k);
+      off[b] = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok0 % BS) * kRowBytes;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      // token 4j + r of the step: block (4j) / BS of the step, row (4j) % BS
+      // inside it when BS < 16, else row 4j after the step's first token
+      constexpr int kStepRows = BS >= 16 ? 16 : BS;
+      const char* kb = a.kslab + off[(4 * j) / kStepRows] + (uint64_t)((4 * j) % kStepRows) * kRowBytes;
+      const char* vb = a.vslab + off[(4 * j) / kStepRows] + (uint64_t)((4 * j) % kStepRows) * kRowBytes;
       if (!tail || tok0 + 4 * j < n) {
 #if PA_NT_LOADS
-        K[j] = nt_load16(kb + j * 4 * kRowBytes + lane_off);
-        V[j] = nt_load16(vb + j * 4 * kRowBytes + lane_off);
+        K[j] = nt_load16(kb + lane_off);
+        V[j] = nt_load16(vb + lane_off);
 #else
-        K[j] = *reinterpret_cast<const uint4*>(kb + j * 4 * kRowBytes + lane_off);
-        V[j] = *reinterpret_cast<const uint4*>(vb + j * 4 * kRowBytes + lane_off);
+        K[j] = *reinterpret_cast<const uint4*>(kb + lane_off);
+        V[j] = *reinterpret_cast<const uint4*>(vb + lane_off);
 #endif
       } else {
         K[j] = make_uint4(0, 0, 0, 0);
@@ -842,7 +859,8 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const int G = Hq / pool->Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
   if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
-  if (pool->B != 16 && pool->B != 32) return fail(PA_ERR_UNSUPPORTED, "block size must be 16 or 32");
+  if (pool->B != 8 && pool->B != 16 && pool->B != 32 && pool->B != 64 && pool->B != 128)
+    return fail(PA_ERR_UNSUPPORTED, "block size must be 8, 16, 32, 64 or 128");
   if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
   if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
@@ -892,10 +910,13 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
-  if (pool->B == 16)
-    ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream);
-  else
-    ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream);
+  switch (pool->B) {
+    case 8: ok = bf16 ? dispatch_g<true, 8>(G, args, grid, stream) : dispatch_g<false, 8>(G, args, grid, stream); break;
+    case 16: ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream); break;
+    case 32: ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream); break;
+    case 64: ok = bf16 ? dispatch_g<true, 64>(G, args, grid, stream) : dispatch_g<false, 64>(G, args, grid, stream); break;
+    default: ok = bf16 ? dispatch_g<true, 128>(G, args, grid, stream) : dispatch_g<false, 128>(G, args, grid, stream); break;
+  }
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
   return hip_check(hipGetLastError(), "decode attention launch");
 }

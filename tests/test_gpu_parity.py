@@ -20,7 +20,7 @@ from oracle.replay import build_state, decode_step
 from tests.harness import (OracleSide, fill_pool_nan, fill_pool_random, layer_inputs, make_engine,
                            replay_history_device, snapshot_layers, to_device_bits, to_host_bits,
                            to_host_f64, tol_stats, within_tolerance)
-from workloads import make_workload, normal_bits, round_to_dtype_bits
+from workloads import make_workload, normal_bits, round_to_dtype_bits, with_headroom
 from workloads.gen import dtype_nan_bits
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,8 @@ def _pool(L, Hkv, B, P, dtype, order=None):
 # --------------------------------------------------------------------------------
 # write_kv and copy_blocks: bit-exact
 # --------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,B,Hkv", [("f16", 16, 2), ("bf16", 32, 8), ("f16", 16, 40)])
+@pytest.mark.parametrize("dtype,B,Hkv", [("f16", 16, 2), ("bf16", 32, 8), ("f16", 16, 40), ("bf16", 8, 4),
+                                         ("f16", 128, 2)])
 def test_write_kv_bit_exact(dtype, B, Hkv):
     _say(f"write_kv {dtype} B={B} Hkv={Hkv}")
     rng = np.random.default_rng(1)
@@ -72,7 +73,8 @@ def test_write_kv_bit_exact(dtype, B, Hkv):
         assert np.array_equal(to_host_bits(pool.slab(l, "v")), host.V[l])
 
 
-@pytest.mark.parametrize("dtype,B,Hkv,L", [("f16", 32, 2, 1), ("f16", 16, 40, 3), ("bf16", 16, 8, 2)])
+@pytest.mark.parametrize("dtype,B,Hkv,L", [("f16", 32, 2, 1), ("f16", 16, 40, 3), ("bf16", 16, 8, 2),
+                                           ("bf16", 8, 4, 2), ("f16", 128, 2, 2)])
 def test_copy_blocks_bit_exact(dtype, B, Hkv, L):
     _say(f"copy_blocks {dtype} B={B} Hkv={Hkv} L={L}")
     rng = np.random.default_rng(2)
@@ -94,8 +96,8 @@ def test_copy_blocks_bit_exact(dtype, B, Hkv, L):
 # --------------------------------------------------------------------------------
 # decode attention on the small workloads: full step vs oracle
 # --------------------------------------------------------------------------------
-def _small_workload_step(cfg, steps=1, fused=True):
-    wl = make_workload(cfg)
+def _small_workload_step(cfg, steps=1, fused=True, block_size=None):
+    wl = with_headroom(make_workload(cfg, block_size=block_size), steps)
     c = wl.cfg
     eng = make_engine(wl, steps=steps, fused=fused)
     fill_pool_nan(eng, c.dtype)                 # unwritten slots hold NaN
@@ -230,6 +232,9 @@ SHAPES = [
     # (G, Hkv, B, dtype)
     (1, 4, 16, "f16"), (2, 2, 16, "bf16"), (4, 2, 16, "f16"), (8, 1, 16, "bf16"),
     (1, 2, 32, "bf16"), (2, 4, 32, "f16"), (4, 8, 32, "bf16"), (8, 2, 32, "f16"),
+    (1, 4, 8, "f16"), (4, 2, 8, "bf16"), (8, 1, 8, "f16"),
+    (2, 2, 64, "bf16"), (4, 8, 64, "f16"),
+    (1, 2, 128, "bf16"), (4, 2, 128, "f16"), (8, 2, 128, "bf16"),
 ]
 
 
@@ -240,6 +245,7 @@ def test_decode_shapes_ragged_lengths(G, Hkv, B, dtype):
     lens = [1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 511, 1000, 1537, 2048, 3001]
     if B == 32:
         lens = lens + [32, 63, 4096]
+    lens = lens + [B - 1, B, B + 1, 2 * B + 3]   # around this block size's boundaries
     S = len(lens)
     Hq = G * Hkv
     pool, host, tables, q = _direct_case(rng, S, Hq, Hkv, B, dtype, lens)
@@ -325,8 +331,8 @@ def test_decode_matches_contiguous_baseline():
 # --------------------------------------------------------------------------------
 # full-size workloads: sampled outputs, in the bench's launch configuration
 # --------------------------------------------------------------------------------
-def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True):
-    wl = make_workload(cfg)
+def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=None):
+    wl = with_headroom(make_workload(cfg, block_size=block_size), steps)
     c = wl.cfg
     eng = make_engine(wl, steps=steps, fused=fused)
     _say(f"config {cfg}: pool {eng.pool.nbytes / 2**30:.1f} GiB, P={wl.P}, S={wl.S}")
@@ -377,6 +383,35 @@ def test_config4_full_size_sampled():
 
 def test_config5_full_size_sampled():
     _full_size(5, steps=2, layers=[0, 39], seqs_per_layer=6, seed=50)
+
+
+@pytest.mark.parametrize("B", [8, 32, 64, 128])
+def test_config3_other_block_sizes_sampled(B):
+    """The config-3 batch stored in blocks of B tokens (block-size sweep)."""
+    _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=4, seed=60 + B, block_size=B)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_small_workloads_at_every_block_size(cfg):
+    """Each block size: full parity with the oracle over two fused steps, the
+    oracle's slots and copies, and outputs bitwise equal to every other block
+    size (the kernel's accumulation order depends on 16-token steps and
+    partitions only, never on where blocks start)."""
+    base = None
+    for B in (8, 16, 32, 64, 128):
+        _say(f"config {cfg} at B={B}")
+        wl, eng, st, results = _small_workload_step(cfg, steps=2, fused=True, block_size=B)
+        outs = []
+        for got, ref, pairs in results:
+            ok, stats = within_tolerance(got, ref)
+            assert ok, (B, stats)
+            outs.append(got)
+        outs = np.stack(outs)
+        if base is None:
+            base = outs
+        else:
+            assert np.array_equal(outs, base), B
+        del eng
 
 
 @pytest.mark.parametrize("cfg,steps", [(1, 2), (2, 2), (5, 1)])

@@ -13,7 +13,9 @@ blocks); each side replays it with its own block manager.
 
 from __future__ import annotations
 
+import dataclasses
 import math
+import re
 from dataclasses import dataclass
 from typing import List, Tuple
 
@@ -214,9 +216,27 @@ def with_headroom(wl: Workload, steps: int) -> Workload:
                     history=wl.history, scale=wl.scale)
 
 
-def make_workload(cfg_id: int) -> Workload:
+def _at_block_size(c: DecodeConfig, B: int, lengths0: np.ndarray) -> DecodeConfig:
+    """``c`` at block size ``B``; seeds, lengths and values are unchanged.  A
+    fixed pool keeps its ratio of pool blocks to used blocks (rounded up)."""
+    name = re.sub(r"_b\d+", f"_b{B}", c.name, count=1)
+    if name == c.name:
+        name = f"{c.name}_b{B}"
+    kw = {"B": int(B), "name": name}
+    if c.pool_kind == "fixed":
+        used_old = int(np.sum(_ceil_div(lengths0, c.B)))
+        used_new = int(np.sum(_ceil_div(lengths0, B)))
+        kw["pool_blocks"] = int(_ceil_div(int(c.pool_blocks) * used_new, used_old))
+    return dataclasses.replace(c, **kw)
+
+
+def make_workload(cfg_id: int, block_size: int | None = None) -> Workload:
+    """Workload ``cfg_id``; ``block_size`` runs the same sequences, history and
+    values over blocks of another size."""
     c = get_config(cfg_id)
     lengths0 = _lengths(c)
+    if block_size is not None and int(block_size) != c.B:
+        c = _at_block_size(c, int(block_size), lengths0)
     assert lengths0.shape[0] == c.S
     P = _pool_blocks(c, lengths0)
     perm = rng_for(c.cfg_id, 0, P_PERM).permutation(P).astype(np.int32)
