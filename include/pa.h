@@ -175,6 +175,27 @@ pa_status pa_seq_fork(pa_pool* pool, const int32_t* parent_table,
  * zero. */
 pa_status pa_seq_free(pa_pool* pool, const int32_t* table, int32_t n_tokens);
 
+/* Beam selection ("vLLM PagedAttention and continuous batching", section
+ * "Sharing with reference counts and copy-on-write": candidates that leave
+ * the beam drop their references, blocks at zero are released, survivors
+ * keep sharing what they share).  New sequence i continues old sequence
+ * parents[i]: it maps the first ceil(lens[parents[i]] / B) blocks of that
+ * table with one more reference each (a fork, i = 0 .. S_new-1 in order);
+ * then every old table is freed (old sequences 0 .. S_old-1 in order, each
+ * table's entries in order, a block reaching zero going to the free list's
+ * tail).  The copy-on-write of shared last blocks happens at the next
+ * append.
+ *   tables: host [S_old][maxb]; lens: host [S_old]; parents: host [S_new],
+ *   each in [0, S_old); out_tables: host [S_new][maxb], must not overlap
+ *   tables (entries past the mapped ones are set to -1); out_lens: host
+ *   [S_new].  S_old = 0 or S_new = 0 are allowed.
+ * INVALID_ARG (and nothing changes) for a parent out of range, a table entry
+ * outside the pool, or a block with fewer references than the old tables
+ * hold. */
+pa_status pa_seq_reorder(pa_pool* pool, const int32_t* tables, const int32_t* lens,
+                         int32_t S_old, int32_t maxb, const int32_t* parents,
+                         int32_t S_new, int32_t* out_tables, int32_t* out_lens);
+
 /* ---------------------------------------------------------------------
  * Device operations ("fused block operations" of the reading guide
  * "Efficient Memory Management for Large Language Model Serving with

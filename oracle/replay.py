@@ -66,6 +66,25 @@ def manager_step(st: OracleState) -> Tuple[List[int], List[Tuple[int, int]], Lis
     return slots, pairs, list(st.lens)
 
 
+def beam_reorder(st: OracleState, parents: Sequence[int]) -> None:
+    """Beam selection before a step ("vLLM PagedAttention and continuous
+    batching", section "Sharing with reference counts and copy-on-write"):
+    each new sequence forks the old sequence it continues (one more reference
+    to each of its blocks), then every old sequence is freed (one fewer;
+    blocks reaching zero are released).  Shared last blocks are copied at the
+    next append, by the usual rule."""
+    maxb = len(st.tables[0]) if st.tables else 0
+    new_tables, new_lens = [], []
+    for par in parents:
+        par = int(par)
+        child = st.mgr.fork(st.tables[par], st.lens[par])
+        new_tables.append(child + [-1] * (maxb - len(child)))
+        new_lens.append(st.lens[par])
+    for table, n in zip(st.tables, st.lens):
+        st.mgr.free_seq(table, n)
+    st.tables, st.lens = new_tables, new_lens
+
+
 def decode_step(st: OracleState, wl, step: int = 0) -> Tuple[np.ndarray, List[int], List[Tuple[int, int]]]:
     """Manager step, block copies, per-layer write of the new token and dense
     attention.  Returns (out [len(layers)][S][Hq][d] float64, slots, pairs)."""

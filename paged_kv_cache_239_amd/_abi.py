@@ -79,6 +79,7 @@ HOST_SIGNATURES = {
     "pa_append_batch": (C.c_int, [P, PI32, I32, PI32, I32, PI64, PI32, PI32, PI32]),
     "pa_seq_fork": (C.c_int, [P, PI32, I32, PI32, I32]),
     "pa_seq_free": (C.c_int, [P, PI32, I32]),
+    "pa_seq_reorder": (C.c_int, [P, PI32, PI32, I32, I32, PI32, I32, PI32, PI32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
 }

@@ -38,7 +38,7 @@ def _run(cmd):
 
 
 def build_hip(extra=()):
-    srcs = [os.path.join(CSRC, "pa_host.cpp"), os.path.join(CSRC, "pa_device.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("pa_host.cpp", "pa_attention.hip", "pa_cache.hip")]
     tmp = LIB + ".tmp"
     _run([HIPCC, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp])
     os.replace(tmp, LIB)

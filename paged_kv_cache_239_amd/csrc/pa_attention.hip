@@ -1,8 +1,7 @@
-// Device side of the paged key/value cache for gfx950 (CDNA4, wave64):
-//   - write_kv     : scatter each new token's keys/values into its slot
-//   - copy_blocks  : whole-block copies for copy-on-write
-//   - decode attn  : single-query attention over block tables, split into
-//                    context partitions merged by the online-softmax rescale
+// Paged decode attention for gfx950 (CDNA4, wave64): single-query attention
+// over block tables, split into context partitions merged by the
+// online-softmax rescale, optionally with the step's cache write fused in.
+// (The cache write and block copies on their own are in pa_cache.hip.)
 //
 // Sources (page title, section):
 //   "vLLM PagedAttention and continuous batching" -- "PagedAttention: fixed
@@ -48,21 +47,15 @@
 //     partials visible across the chip's L2 caches without a device-scope
 //     fence per workgroup (such a fence writes back a whole L2).
 
-#include <hip/hip_runtime.h>
-
 #include <cmath>
-#include <cstdint>
-#include <cstdlib>
 #include <string>
 
-#include "pa_internal.h"
+#include "pa_device_common.h"
 
 using pa_detail::fail;
 
 namespace {
 
-constexpr int kD = 128;            // head dimension of every compiled kernel
-constexpr int kRowBytes = kD * 2;  // one token of one head: 256 bytes
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest kept weight
 
 // Key/value tiles are read once per step: load them with the streaming
@@ -70,14 +63,6 @@ constexpr float kRescaleSlack = 8.0f;  // log2 of the largest kept weight
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1
 #endif
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte load with the non-temporal (streaming) cache hint
-__device__ __forceinline__ uint4 nt_load16(const char* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -342,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   // groups of 16 tokens in this partition, dealt round-robin to the waves:
   // the k-th group of this wave is g_first + k * NW, and lane k holds that
   // group's physical block (one lane read per group later).
-  const int g_full = t_end / 16;               // groups [.., g_full) are full
+  int g_full = t_end / 16;                     // groups [.., g_full) are full
   const int g_last = (t_end + 15) / 16;        // a tail group exists if g_full < g_last
   uint4 qr[G];
   int my_phys[BPG];
@@ -387,6 +372,11 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     }
   }
 
+  // The step holding position n-1 is the partition's last one; it always
+  // takes the peeled tail path, so the substitution above costs nothing in
+  // the main loop.
+  if (g_new >= 0) g_full = g_new;
+
   auto load_group = [&](int k, uint4 (&K)[4], uint4 (&V)[4], bool tail) {
     const int g = g_first + k * NW;
     const int tok0 = g * 16;
@@ -427,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
       K[j] = Kin[j];
       V[j] = Vin[j];
     }
-    if (g == g_new) {
+    if (tail && g == g_new) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (j == j_new && r == r_new) {
@@ -697,63 +687,6 @@ __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a
   *out_row = narrow8<BF16>(o);
 }
 
-// ---------------------------------------------------------------------------
-// write_kv: one workgroup per token
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void write_kv_kernel(char* kslab, char* vslab, const uint4* k, const uint4* v,
-                                                       const int64_t* slots, int Hkv, int B, int64_t nslots,
-                                                       uint64_t tile_bytes) {
-  const int s = blockIdx.x;
-  const int64_t slot = slots[s];
-  if (slot < 0 || slot >= nslots) return;
-  const int64_t blk = slot / B;
-  const int off = (int)(slot % B);
-  const int chunks_per_row = kRowBytes / 16;  // 16
-  const int chunks = Hkv * chunks_per_row;
-  for (int i = threadIdx.x; i < chunks; i += blockDim.x) {
-    const int h = i / chunks_per_row;
-    const int w = i % chunks_per_row;
-    const uint64_t dst = (uint64_t)blk * tile_bytes + ((uint64_t)h * B + off) * kRowBytes + (uint64_t)w * 16;
-    *reinterpret_cast<uint4*>(kslab + dst) = k[(size_t)s * chunks + i];
-    *reinterpret_cast<uint4*>(vslab + dst) = v[(size_t)s * chunks + i];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// copy_blocks: one workgroup per (pair, slab); it streams the whole tile with
-// kCopyUnroll 16-byte non-temporal loads per thread in flight
-// ---------------------------------------------------------------------------
-constexpr int kCopyUnroll = 8;
-constexpr int kCopyThreads = 256;
-
-__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* base, const int32_t* pairs, int P,
-                                                                   uint64_t tile_bytes, uint64_t slab_bytes) {
-  const int pr = blockIdx.y;
-  const int32_t src = pairs[2 * pr];
-  const int32_t dst = pairs[2 * pr + 1];
-  if (src < 0 || src >= P || dst < 0 || dst >= P || src == dst) return;
-  char* slab = base + (uint64_t)blockIdx.x * slab_bytes;
-  const char* from = slab + (uint64_t)src * tile_bytes;
-  char* to = slab + (uint64_t)dst * tile_bytes;
-  const uint64_t nchunks = tile_bytes / 16;
-  for (uint64_t first = threadIdx.x; first < nchunks; first += (uint64_t)kCopyThreads * kCopyUnroll) {
-    uint4 tmp[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const uint64_t i = first + (uint64_t)u * kCopyThreads;
-      if (i < nchunks) tmp[u] = nt_load16(from + i * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const uint64_t i = first + (uint64_t)u * kCopyThreads;
-      if (i < nchunks) {
-        const u32x4_t v = {tmp[u].x, tmp[u].y, tmp[u].z, tmp[u].w};
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(to + i * 16));
-      }
-    }
-  }
-}
-
 __global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntail) {
   const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -773,12 +706,6 @@ struct LaunchCfg {
   int part_tokens = 0;
   int nparts_max = 1;
 };
-
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  return std::atoi(v);
-}
 
 // Partition length: as long as possible (fewer partials to merge) while the
 // grid still has several workgroups per compute unit.
@@ -818,11 +745,6 @@ WsLayout ws_layout(int S, int Hkv, int G, const LaunchCfg& cfg) {
   return w;
 }
 
-pa_status hip_check(hipError_t e, const char* what) {
-  if (e == hipSuccess) return PA_OK;
-  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
 template <bool BF16, int G, int BS>
 void launch_decode(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
@@ -840,8 +762,6 @@ bool dispatch_g(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
     default: return false;
   }
 }
-
-bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 }  // namespace
 
@@ -924,38 +844,6 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
 }  // namespace
 
 extern "C" {
-
-pa_status pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v, const int64_t* slot_mapping, int S,
-                      hipStream_t stream) {
-  pa_detail::clear_error();
-  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
-  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
-  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
-  if (S == 0) return PA_OK;
-  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
-  if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
-    return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
-  if (S > 2147483647) return fail(PA_ERR_INVALID_ARG, "S too large");
-  hipLaunchKernelGGL(write_kv_kernel, dim3(S), dim3(256), 0, stream, pool->k_slab(layer), pool->v_slab(layer),
-                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping, pool->Hkv, pool->B,
-                     (int64_t)pool->P * pool->B, (uint64_t)pool->tile_bytes);
-  return hip_check(hipGetLastError(), "write_kv launch");
-}
-
-pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N, hipStream_t stream) {
-  pa_detail::clear_error();
-  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
-  if (N < 0) return fail(PA_ERR_INVALID_ARG, "negative N");
-  if (N == 0) return PA_OK;
-  if (!pairs || !aligned(pairs, 4)) return fail(PA_ERR_INVALID_ARG, "pairs must be a 4-byte aligned device pointer");
-  if (N > 65535) return fail(PA_ERR_INVALID_ARG, "at most 65535 pairs per call");
-  if (pool->tile_bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block size in bytes must be a multiple of 16");
-  const dim3 grid((unsigned)(2 * pool->L), (unsigned)N);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, pool->base, pairs, pool->P,
-                     (uint64_t)pool->tile_bytes, (uint64_t)pool->slab_bytes);
-  return hip_check(hipGetLastError(), "copy_blocks launch");
-}
 
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx) {
   if (!pool || S <= 0 || Hq <= 0 || max_ctx < 0 || Hq % pool->Hkv) return 0;

@@ -400,4 +400,58 @@ pa_status pa_seq_free(pa_pool* pool, const int32_t* table, int32_t n_tokens) {
   return PA_OK;
 }
 
+pa_status pa_seq_reorder(pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t S_old, int32_t maxb,
+                         const int32_t* parents, int32_t S_new, int32_t* out_tables, int32_t* out_lens) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (S_old < 0 || S_new < 0 || maxb < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (S_new > 0 && S_old == 0) return fail(PA_ERR_INVALID_ARG, "no sequence to continue");
+  if (S_old > 0 && (!tables || !lens)) return fail(PA_ERR_INVALID_ARG, "NULL old tables or lengths");
+  if (S_new > 0 && (!parents || !out_tables || !out_lens)) return fail(PA_ERR_INVALID_ARG, "NULL new arrays");
+  if (S_new > 0 && S_old > 0 && maxb > 0) {
+    const char* a0 = reinterpret_cast<const char*>(tables);
+    const char* a1 = a0 + (size_t)S_old * maxb * sizeof(int32_t);
+    const char* b0 = reinterpret_cast<const char*>(out_tables);
+    const char* b1 = b0 + (size_t)S_new * maxb * sizeof(int32_t);
+    if (a0 < b1 && b0 < a1) return fail(PA_ERR_INVALID_ARG, "out_tables overlaps tables");
+  }
+  // validate everything first: parents, lengths, entries, and that the old
+  // tables do not hold more references to a block than it has
+  std::vector<int32_t> held((size_t)pool->P, 0);
+  for (int32_t s = 0; s < S_old; ++s) {
+    const int64_t nb = ((int64_t)lens[s] + pool->B - 1) / pool->B;
+    if (lens[s] < 0 || nb > maxb) return fail(PA_ERR_INVALID_ARG, "length outside the table");
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = tables[(size_t)s * maxb + j];
+      if (!in_range(pool, b)) return fail(PA_ERR_INVALID_ARG, "table entry outside the pool");
+      held[(size_t)b] += 1;
+    }
+  }
+  for (int32_t b = 0; b < pool->P; ++b)
+    if (held[(size_t)b] > pool->ref[(size_t)b])
+      return fail(PA_ERR_INVALID_ARG, "block has fewer references than the tables hold");
+  for (int32_t i = 0; i < S_new; ++i)
+    if (parents[i] < 0 || parents[i] >= S_old) return fail(PA_ERR_INVALID_ARG, "parent out of range");
+  // forks, in new-sequence order
+  for (int32_t i = 0; i < S_new; ++i) {
+    const int32_t par = parents[i];
+    const int32_t n = lens[par];
+    const int32_t nb = (int32_t)(((int64_t)n + pool->B - 1) / pool->B);
+    const int32_t* src = tables + (size_t)par * maxb;
+    int32_t* dst = out_tables + (size_t)i * maxb;
+    for (int32_t j = 0; j < nb; ++j) {
+      pool->ref[(size_t)src[j]] += 1;
+      dst[j] = src[j];
+    }
+    for (int32_t j = nb; j < maxb; ++j) dst[j] = -1;
+    out_lens[i] = n;
+  }
+  // frees, in old-sequence order
+  for (int32_t s = 0; s < S_old; ++s) {
+    const int32_t nb = (int32_t)(((int64_t)lens[s] + pool->B - 1) / pool->B);
+    for (int32_t j = 0; j < nb; ++j) do_decref(pool, tables[(size_t)s * maxb + j]);
+  }
+  return PA_OK;
+}
+
 }  // extern "C"

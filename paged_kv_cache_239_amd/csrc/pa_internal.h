@@ -1,5 +1,5 @@
 // Internal definitions shared by the host manager (pa_host.cpp) and the
-// device launchers (pa_device.hip).  Not part of the public ABI.
+// device launchers (pa_attention.hip, pa_cache.hip).  Not part of the public ABI.
 #pragma once
 
 #include <cstddef>

@@ -86,6 +86,13 @@ class DecodeEngine:
         self.pool.fork(self.tables[parent], ntok, self.tables[child])
         self.lens[child] = ntok
 
+    def reorder(self, parents) -> None:
+        """Beam selection before a step: sequence i continues old sequence
+        parents[i]; the old tables are released (pa_seq_reorder)."""
+        tables, lens = self.pool.seq_reorder(self.tables, self.lens, parents)
+        self.tables[:] = tables
+        self.lens[:] = lens
+
     def upload_tables(self, stream=None) -> None:
         """Synchronous upload of the current tables and lengths."""
         torch = self.torch

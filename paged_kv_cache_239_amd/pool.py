@@ -185,6 +185,21 @@ class Pool:
         assert table.dtype == np.int32
         check(self.lib, self.lib.pa_seq_free(self.handle, _i32p(table), int(n_tokens)))
 
+    def seq_reorder(self, tables: np.ndarray, lens: np.ndarray, parents) -> Tuple[np.ndarray, np.ndarray]:
+        """Beam selection: new sequence i continues old sequence parents[i]
+        (fork), then every old table is freed.  Returns (new tables int32
+        [S_new][maxb], new lengths int32 [S_new])."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
+        S_old, maxb = tables.shape
+        ln = _as_i32(lens)
+        par = _as_i32(parents)
+        S_new = int(par.shape[0])
+        out = np.empty((max(S_new, 1), maxb), dtype=np.int32)
+        out_lens = np.empty(max(S_new, 1), dtype=np.int32)
+        check(self.lib, self.lib.pa_seq_reorder(self.handle, _i32p(tables), _i32p(ln), S_old, maxb, _i32p(par), S_new,
+                                                _i32p(out), _i32p(out_lens)))
+        return out[:S_new], out_lens[:S_new]
+
     # ---- device operations -------------------------------------------------------
     def write_kv(self, layer: int, k, v, slot_mapping, stream=None) -> None:
         """k, v: device [S][Hkv][d] of the pool dtype; slot_mapping: device int64 [S]."""

@@ -15,7 +15,7 @@ import numpy as np
 
 from oracle.cache_ops import HostPool, copy_blocks, write_kv
 from oracle.decode import decode_one
-from oracle.replay import build_state, manager_step
+from oracle.replay import beam_reorder, build_state, manager_step
 from workloads import make_workload
 from workloads.gen import dtype_nan_bits
 
@@ -149,6 +149,8 @@ class OracleSide:
         self.pools = snapshots
 
     def step(self, step: int):
+        if self.wl.cfg.beam:
+            beam_reorder(self.state, self.wl.parents(step))
         slots, pairs, lens = manager_step(self.state)
         for layer, pool in self.pools.items():
             copy_blocks(pool, pairs)

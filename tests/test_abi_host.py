@@ -11,7 +11,7 @@ import pytest
 
 from oracle.manager import BlockManager, InvalidArg
 from oracle.manager import OutOfBlocks as OracleOOB
-from oracle.replay import build_state, manager_step
+from oracle.replay import beam_reorder, build_state, manager_step
 from paged_kv_cache_239_amd import _abi
 from paged_kv_cache_239_amd.pool import Pool
 from workloads import make_workload
@@ -73,7 +73,7 @@ def test_manager_bit_exact_random_traces(seed):
     o_tables, o_lens = [], []
     n_tables = [[] for _ in natives]
     for step in range(250):
-        op = int(rng.integers(0, 5))
+        op = int(rng.integers(0, 6))
         if op == 0 or not o_tables:                       # new sequence, prefill
             n = int(rng.integers(0, 3 * B + 1))
             ot = [-1] * maxb
@@ -139,6 +139,24 @@ def test_manager_bit_exact_random_traces(seed):
                 n_tables[k].pop(i)
             o_tables.pop(i)
             o_lens.pop(i)
+        elif op == 5:                                        # beam selection over all sequences
+            if not o_tables:
+                continue
+            S_new = int(rng.integers(0, len(o_tables) + 2))
+            parents = rng.integers(0, len(o_tables), size=S_new).astype(np.int32)
+            o_new, o_new_lens = [], []
+            for par in parents:
+                child = ora.fork(o_tables[par], o_lens[par])
+                o_new.append(child + [-1] * (maxb - len(child)))
+                o_new_lens.append(o_lens[par])
+            for t, n in zip(o_tables, o_lens):
+                ora.free_seq(t, n)
+            for k, pool in enumerate(natives):
+                tabs = np.stack(n_tables[k]).astype(np.int32)
+                new_tabs, new_lens = pool.seq_reorder(tabs, np.array(o_lens, dtype=np.int32), parents)
+                assert list(new_lens) == o_new_lens
+                n_tables[k] = [row.copy() for row in new_tabs]
+            o_tables, o_lens = o_new, o_new_lens
         else:                                                # single append to one sequence
             i = int(rng.integers(len(o_tables)))
             if o_lens[i] >= maxb * B:
@@ -193,10 +211,10 @@ def test_error_paths_match_oracle():
     assert (pool.refcounts(), pool.free_list()) == before[:2] and np.array_equal(t, before[2])
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_workload_histories_bit_exact(cfg):
     wl = make_workload(cfg)
-    steps = 3 if cfg != 4 else 1
+    steps = {4: 1, 6: wl.cfg.steps}.get(cfg, 3)
     maxb = wl.max_blocks(steps)
     st = build_state(wl, maxb=maxb)
     pool = Pool(1, 1, 128, wl.cfg.B, wl.P, "f16", free_order=wl.free_order, device=None, host_only_lib=True)
@@ -213,6 +231,13 @@ def test_workload_histories_bit_exact(cfg):
             lens[child] = n
     assert list(lens) == st.lens
     for step in range(steps):
+        if wl.cfg.beam:
+            parents = wl.parents(step)
+            beam_reorder(st, parents)
+            tables, lens = pool.seq_reorder(tables, lens, parents)
+            tables, lens = tables.copy(), lens.copy()
+            assert pool.refcounts() == st.mgr.ref
+            assert pool.free_list() == st.mgr.free_list()
         o_slots, o_pairs, _ = manager_step(st)
         slots, pairs = pool.append_batch(tables, lens)
         lens += 1

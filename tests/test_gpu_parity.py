@@ -346,6 +346,8 @@ def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=
     for step in range(steps):
         qs, ks, vs = layer_inputs(wl, range(c.L), step)
         outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+        if c.beam:
+            eng.reorder(wl.parents(step))
         max_ctx = eng.manager_step()
         eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
         torch.cuda.synchronize()
@@ -385,6 +387,12 @@ def test_config5_full_size_sampled():
     _full_size(5, steps=2, layers=[0, 39], seqs_per_layer=6, seed=50)
 
 
+def test_config6_beam_search_sampled():
+    """Beam reselection before every step: forks, frees, copy-on-write of
+    shared last blocks, then the fused write and attention."""
+    _full_size(6, steps=4, layers=[0, 39], seqs_per_layer=8, seed=66)
+
+
 @pytest.mark.parametrize("B", [8, 32, 64, 128])
 def test_config3_other_block_sizes_sampled(B):
     """The config-3 batch stored in blocks of B tokens (block-size sweep)."""
@@ -414,7 +422,7 @@ def test_small_workloads_at_every_block_size(cfg):
         del eng
 
 
-@pytest.mark.parametrize("cfg,steps", [(1, 2), (2, 2), (5, 1)])
+@pytest.mark.parametrize("cfg,steps", [(1, 2), (2, 2), (5, 1), (6, 2)])
 def test_fused_write_attention_equals_separate_calls(cfg, steps):
     """pa_write_kv_decode_attention == pa_write_kv then pa_decode_attention:
     outputs and the whole pool byte for byte."""
@@ -424,7 +432,7 @@ def test_fused_write_attention_equals_separate_calls(cfg, steps):
     engines = []
     for fused in (True, False):
         eng = make_engine(wl, steps=steps, fused=fused)
-        if cfg == 5:
+        if cfg in (5, 6):
             fill_pool_random(eng, wl)
             replay_history_device(eng, wl, write_values=False)
         else:
@@ -436,6 +444,8 @@ def test_fused_write_attention_equals_separate_calls(cfg, steps):
         outs = []
         for eng in engines:
             o = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+            if c.beam:
+                eng.reorder(wl.parents(step))
             max_ctx = eng.manager_step()
             eng.device_step(qs, ks, vs, o, max_ctx, float(wl.scale))
             outs.append(o)

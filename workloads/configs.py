@@ -1,4 +1,4 @@
-"""The five decode workloads, as plain parameters.
+"""The decode workloads, as plain parameters.
 
 Shapes follow the pages' statement of the problem: L layers, H_kv key/value
 heads, head dimension d, block size B, b bytes per stored scalar ("Serving
@@ -46,6 +46,7 @@ class DecodeConfig:
     max_len: int = 0
     steps: int = 1                      # decode steps the workload runs
     share_prefix_tokens: int = 0        # cfg2: tokens of seq 0 mapped by seqs 1..S-1
+    beam: bool = False                  # lognormal_branches: reselect the branches every step
     description: str = field(default="", compare=False)
 
     @property
@@ -96,6 +97,17 @@ CONFIGS = {
                     "64 prompts x 4 sampled branches sharing prompt blocks, "
                     "log-normal prompt lengths (median 300, max 2048), B=16, "
                     "32 decode steps with copy-on-write"),
+    6: DecodeConfig(
+        cfg_id=6, name="opt13b_shape_mha40_f16_b16_beam4",
+        L=40, Hq=40, Hkv=40, d=128, B=16, dtype="f16",
+        length_kind="lognormal_branches", S=256, prompts=64, branches=4,
+        lognormal_median=300.0, lognormal_sigma=0.8, max_len=2048, steps=32,
+        pool_kind="branch_bound", beam=True,
+        description="beam search of width 4 over config 5's shape: before every "
+                    "step each prompt's 4 beams are reselected from its current "
+                    "beams (seeded parents, better beams more likely), dropped "
+                    "beams release their blocks, shared last blocks are copied "
+                    "on write"),
 }
 
 

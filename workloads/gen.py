@@ -33,6 +33,7 @@ P_PREFILL_K = 6
 P_PREFILL_V = 7
 P_POOL_K = 8
 P_POOL_V = 9
+P_PARENTS = 10
 
 SEED_ROOT = 239
 
@@ -113,6 +114,20 @@ class Workload:
         c = self.cfg
         purpose = P_PREFILL_K if which == "k" else P_PREFILL_V
         return normal_bits(rng_for(c.cfg_id, layer, purpose, op_index), (ntok, c.Hkv, c.d), c.dtype)
+
+    def parents(self, step: int) -> np.ndarray:
+        """Beam workloads: int32 [S], the old sequence each new sequence
+        continues at ``step``.  Per prompt, W draws from its W beams with
+        probabilities proportional to W, W-1, ..., 1 (beam j of a prompt
+        stands for its j-th best candidate), sorted, so a prompt's beams stay
+        together and some beams end while others split."""
+        c = self.cfg
+        W = c.branches
+        r = rng_for(c.cfg_id, 0, P_PARENTS, step)
+        w = np.arange(W, 0, -1, dtype=np.float64)
+        draws = r.choice(W, size=(c.prompts, W), p=w / w.sum())
+        draws.sort(axis=1)
+        return (np.arange(c.prompts)[:, None] * W + draws).reshape(-1).astype(np.int32)
 
     def pool_fill_seed(self, layer: int, which: str) -> int:
         """Seed for filling a whole layer slab in device memory (large workloads)."""
