@@ -141,6 +141,9 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=0,
                     help="store the workload in blocks of this many tokens (8, 16, 32, 64 or 128; "
                          "default: the workload's own)")
+    ap.add_argument("--swap", type=int, default=0, metavar="N",
+                    help="instead of decode steps: swap the first N sequences of the workload out to a "
+                         "pinned host pool and back, and time it")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
@@ -174,6 +177,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel() * 4, "copies": 3}))
         return 0
+
+    if args.swap:
+        return swap_bench(args)
 
     W, K = args.warmup, args.steps
     wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
@@ -398,6 +404,119 @@ def main() -> int:
         result["cpu_baseline"], result["parity"] = cpu_baseline(wl, eng, snaps, outs, W + K, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def swap_bench(args) -> int:
+    """Preemption by swapping: the first N sequences of the workload (all
+    their blocks, every layer) move to a pinned host pool and back, each
+    direction one pa_swap_blocks launch in which the GPU writes or reads host
+    memory directly.  For comparison a sample of the same tiles is copied
+    with one DMA transfer per tile (per layer, keys and values: the many
+    short transfers that small blocks turn a swap into).  Bytes = moved
+    blocks x 2 L tiles; the round trip is checked byte for byte."""
+    import torch
+
+    from paged_kv_cache_239_amd import Pool
+    from paged_kv_cache_239_amd.engine import DecodeEngine
+    from workloads import make_workload
+
+    wl = make_workload(args.config, block_size=args.block_size or None)
+    c = wl.cfg
+    eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(1), free_order=wl.free_order)
+    for layer in range(c.L):
+        for which in ("k", "v"):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(wl.pool_fill_seed(layer, which))
+            eng.pool.slab(layer, which).normal_(generator=g)
+    for op in wl.history:
+        if op[0] == "append":
+            eng.append(op[1], op[2])
+        else:
+            eng.fork(op[1], op[2], op[3])
+    N = min(args.swap, wl.S)
+    group = eng.tables[:N].copy()
+    lens = eng.lens[:N].copy()
+    need = len(np.unique(np.concatenate([group[s, : -(-int(n) // c.B)] for s, n in enumerate(lens)])))
+    host = Pool(c.L, c.Hkv, c.d, c.B, need, c.dtype, device="pinned")
+    dev = eng.pool
+    tile = dev.nbytes // (2 * c.L * wl.P)
+    slab_d, slab_h = wl.P * tile, need * tile
+
+    def tiles_of(pool_buf, slab, blocks):
+        # [2L][n][tile] view of the given blocks of every slab
+        idx = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device=pool_buf.device)
+        v = pool_buf.view(2 * c.L, slab // tile, tile)
+        return v.index_select(1, idx)
+
+    torch.cuda.synchronize()
+    # load the kernel before timing (a pair outside both pools copies nothing)
+    dev.swap_blocks(host, torch.tensor([[wl.P, need]], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    t0 = time.perf_counter()
+    pairs = dev.move_blocks(host, group, lens)
+    t1 = time.perf_counter()
+    before = tiles_of(dev.buffer, slab_d, pairs[:, 0]).clone()
+    d_pairs = torch.from_numpy(pairs).cuda()
+    torch.cuda.synchronize()
+    e[0].record()
+    dev.swap_blocks(host, d_pairs)
+    e[1].record()
+    torch.cuda.synchronize()
+    # the device blocks are free now: overwrite them, as the next user would
+    dv = dev.buffer.view(2 * c.L, wl.P, tile)
+    dv.index_fill_(1, torch.as_tensor(pairs[:, 0].astype(np.int64), device="cuda"), 0)
+    t2 = time.perf_counter()
+    back = host.move_blocks(dev, group, lens)
+    t3 = time.perf_counter()
+    d_back = torch.from_numpy(back).cuda()
+    torch.cuda.synchronize()
+    e[2].record()
+    host.swap_blocks(dev, d_back)
+    e[3].record()
+    torch.cuda.synchronize()
+    # back[i] = (host block, new device block) in the order pairs[i] = (old device block, host block)
+    order = {int(h): i for i, h in enumerate(pairs[:, 1])}
+    perm = np.array([order[int(h)] for h in back[:, 0]])
+    after = tiles_of(dev.buffer, slab_d, back[:, 1])
+    exact = bool(torch.equal(after, before[:, perm]))
+    nbytes = len(pairs) * 2 * c.L * tile
+    out_ms, in_ms = e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
+    # per-tile DMA copies, on a sample of the blocks (device -> host)
+    sample = min(len(pairs), max(1, 4096 // (2 * c.L)))
+    dsrc = dev.buffer.view(2 * c.L, wl.P, tile)
+    hdst = host.buffer.view(2 * c.L, need, tile)
+    torch.cuda.synchronize()
+    e[4].record()
+    for i in range(sample):
+        a, b = int(back[i, 1]), int(back[i, 0])
+        for sl in range(2 * c.L):
+            hdst[sl, b].copy_(dsrc[sl, a], non_blocking=True)
+    e[5].record()
+    torch.cuda.synchronize()
+    dma_ms = e[4].elapsed_time(e[5])
+    dma_bytes = sample * 2 * c.L * tile
+    res = {
+        "metric": "swap GB/s: device pool <-> pinned host pool, one kernel launch per direction",
+        "value": round(nbytes / (out_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: first {N} sequences ({int(lens.sum())} tokens), all {c.L} layers",
+                   "block_size": c.B, "tile_bytes": int(tile), "blocks": int(len(pairs)), "bytes": int(nbytes)},
+        "swap_out_ms": round(out_ms, 3),
+        "swap_in_ms": round(in_ms, 3),
+        "swap_in_gbs": round(nbytes / (in_ms * 1e-3) / 1e9, 2),
+        "host_manager_ms": {"out": round((t1 - t0) * 1e3, 3), "in": round((t3 - t2) * 1e3, 3)},
+        "per_tile_dma": {"tiles": sample * 2 * c.L, "tile_bytes": int(tile), "ms": round(dma_ms, 3),
+                         "gbs": round(dma_bytes / (dma_ms * 1e-3) / 1e9, 2),
+                         "note": "one hipMemcpyAsync per (block, layer, keys or values) tile, device to host"},
+        "round_trip_bit_exact": exact,
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if exact else 1
 
 
 def cpu_baseline(wl, eng, snaps, outs, total_steps, budget_s):

@@ -196,6 +196,29 @@ pa_status pa_seq_reorder(pa_pool* pool, const int32_t* tables, const int32_t* le
                          int32_t S_old, int32_t maxb, const int32_t* parents,
                          int32_t S_new, int32_t* out_tables, int32_t* out_lens);
 
+/* Swap a group of sequences between two pools of the same shape (L, Hkv,
+ * d, B, dtype), e.g. from the device pool to a host pool and back:
+ * preemption by swapping ("vLLM PagedAttention and continuous batching",
+ * section "Preemption when blocks run out": all blocks of a sequence or
+ * none; sequences that share blocks, such as the beams of one search, move
+ * together; the host side has its own block allocator, no larger than the
+ * device pool).  Host manager only; pa_swap_blocks moves the bytes.
+ *   For each distinct block the group's tables name in `from` (in order of
+ *   first appearance: sequence 0's entries, then sequence 1's, ...) one block
+ *   of `to` is allocated and given as many references as the group holds;
+ *   pairs[i] = (old block, new block).  Then the group's references in
+ *   `from` are dropped (sequence by sequence, entry by entry, as by
+ *   pa_seq_free), which releases every moved block.  Finally the tables are
+ *   rewritten in place to name the blocks of `to`.
+ *   tables: host [S][maxb]; lens: host [S]; pairs: host [cap][2];
+ *   *n_pairs = blocks moved.
+ * All or nothing: INVALID_ARG if a block is also mapped outside the group
+ * (its refcount exceeds the group's references), if the shapes differ or cap
+ * is too small; OUT_OF_BLOCKS if `to` has fewer free blocks than needed. */
+pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables,
+                         const int32_t* lens, int32_t S, int32_t maxb,
+                         int32_t* pairs, int32_t cap, int32_t* n_pairs);
+
 /* ---------------------------------------------------------------------
  * Device operations ("fused block operations" of the reading guide
  * "Efficient Memory Management for Large Language Model Serving with
@@ -217,6 +240,20 @@ pa_status pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
  * dst are skipped.  Destinations must be distinct and must not appear as a
  * source in the same call. */
 pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N,
+                         hipStream_t stream);
+
+/* swap_blocks: the bytes of pa_move_blocks.  For each pair (src block of
+ * `from`, dst block of `to`) in pairs (device int32 [N][2]) copy the whole
+ * block -- every layer, keys and values -- from one pool's memory to the
+ * other's.  Each pool's memory is device memory or pinned host memory
+ * allocated with hipHostMalloc (mapped into the device's address space); the
+ * copy is one kernel launch in which the GPU reads or writes host memory
+ * directly over the host link, so a small block costs no transfer of its
+ * own.  Pools must have the same shape; pairs with an id outside either
+ * pool are skipped.  INVALID_ARG if a pool's memory is neither device memory
+ * nor mapped pinned host memory.  Asynchronous on `stream`: host memory is
+ * complete once the stream has been synchronised. */
+pa_status pa_swap_blocks(pa_pool* from, pa_pool* to, const int32_t* pairs, int N,
                          hipStream_t stream);
 
 /* Workspace for pa_decode_attention calls with up to S sequences, Hq query

@@ -80,6 +80,7 @@ HOST_SIGNATURES = {
     "pa_seq_fork": (C.c_int, [P, PI32, I32, PI32, I32]),
     "pa_seq_free": (C.c_int, [P, PI32, I32]),
     "pa_seq_reorder": (C.c_int, [P, PI32, PI32, I32, I32, PI32, I32, PI32, PI32]),
+    "pa_move_blocks": (C.c_int, [P, P, PI32, PI32, I32, I32, PI32, I32, PI32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
 }
@@ -87,6 +88,7 @@ HOST_SIGNATURES = {
 DEVICE_SIGNATURES = {
     "pa_write_kv": (C.c_int, [P, C.c_int, P, P, P, C.c_int, P]),
     "pa_copy_blocks": (C.c_int, [P, P, C.c_int, P]),
+    "pa_swap_blocks": (C.c_int, [P, P, P, C.c_int, P]),
     "pa_decode_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int]),
     "pa_decode_workspace_init": (C.c_int, [P, C.c_size_t, P]),
     "pa_decode_attention": (C.c_int, [P, C.c_int, P, P, C.c_int, C.c_int, P, C.c_int, P, C.c_int,

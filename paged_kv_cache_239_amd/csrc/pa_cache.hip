@@ -70,6 +70,61 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* base, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// swap_blocks: copy_blocks between two pools (one may be pinned host memory,
+// read or written by the GPU through its device-mapped address)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(const char* from, char* to, const int32_t* pairs,
+                                                                   int P_from, int P_to, uint64_t tile_bytes,
+                                                                   uint64_t slab_from, uint64_t slab_to) {
+  const int pr = blockIdx.y;
+  const int32_t src = pairs[2 * pr];
+  const int32_t dst = pairs[2 * pr + 1];
+  if (src < 0 || src >= P_from || dst < 0 || dst >= P_to) return;
+  const char* a = from + (uint64_t)blockIdx.x * slab_from + (uint64_t)src * tile_bytes;
+  char* b = to + (uint64_t)blockIdx.x * slab_to + (uint64_t)dst * tile_bytes;
+  const uint64_t nchunks = tile_bytes / 16;
+  for (uint64_t first = threadIdx.x; first < nchunks; first += (uint64_t)kCopyThreads * kCopyUnroll) {
+    uint4 tmp[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = first + (uint64_t)u * kCopyThreads;
+      if (i < nchunks) tmp[u] = nt_load16(a + i * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = first + (uint64_t)u * kCopyThreads;
+      if (i < nchunks) nt_store16(b + i * 16, tmp[u]);
+    }
+  }
+}
+
+// The address at which kernels reach a pool's memory: the memory itself for
+// device memory, the mapped alias for pinned host memory.
+pa_status device_view(const pa_pool* pool, char** out) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, pool->base);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID_ARG, "pool memory is neither device memory nor pinned host memory");
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = pool->base;
+    return PA_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    // only memory from hipHostMalloc has host-allocation flags
+    unsigned int flags = 0;
+    if (hipHostGetFlags(&flags, pool->base) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID_ARG, "host pool memory was not allocated with hipHostMalloc");
+    }
+    *out = static_cast<char*>(attr.devicePointer);
+    return PA_OK;
+  }
+  return fail(PA_ERR_INVALID_ARG, "pool memory is not mapped into the device's address space");
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +159,26 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int N, hipStream_t
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, pool->base, pairs, pool->P,
                      (uint64_t)pool->tile_bytes, (uint64_t)pool->slab_bytes);
   return hip_check(hipGetLastError(), "copy_blocks launch");
+}
+
+pa_status pa_swap_blocks(pa_pool* from, pa_pool* to, const int32_t* pairs, int N, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (!from || !to) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (from->L != to->L || from->Hkv != to->Hkv || from->d != to->d || from->B != to->B || from->dtype != to->dtype)
+    return fail(PA_ERR_INVALID_ARG, "pools differ in shape");
+  if (N < 0) return fail(PA_ERR_INVALID_ARG, "negative N");
+  if (N == 0) return PA_OK;
+  if (!pairs || !aligned(pairs, 4)) return fail(PA_ERR_INVALID_ARG, "pairs must be a 4-byte aligned device pointer");
+  if (N > 65535) return fail(PA_ERR_INVALID_ARG, "at most 65535 pairs per call");
+  if (from->tile_bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block size in bytes must be a multiple of 16");
+  char* a = nullptr;
+  char* b = nullptr;
+  if (pa_status st = device_view(from, &a)) return st;
+  if (pa_status st = device_view(to, &b)) return st;
+  const dim3 grid((unsigned)(2 * from->L), (unsigned)N);
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, a, b, pairs, from->P, to->P,
+                     (uint64_t)from->tile_bytes, (uint64_t)from->slab_bytes, (uint64_t)to->slab_bytes);
+  return hip_check(hipGetLastError(), "swap_blocks launch");
 }
 
 }  // extern "C"

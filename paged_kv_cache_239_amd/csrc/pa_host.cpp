@@ -454,4 +454,59 @@ pa_status pa_seq_reorder(pa_pool* pool, const int32_t* tables, const int32_t* le
   return PA_OK;
 }
 
+pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables, const int32_t* lens, int32_t S, int32_t maxb,
+                         int32_t* pairs, int32_t cap, int32_t* n_pairs) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(from)) return st;
+  if (pa_status st = check_pool(to)) return st;
+  if (from == to) return fail(PA_ERR_INVALID_ARG, "from and to are the same pool");
+  if (from->L != to->L || from->Hkv != to->Hkv || from->d != to->d || from->B != to->B || from->dtype != to->dtype)
+    return fail(PA_ERR_INVALID_ARG, "pools differ in shape");
+  if (!n_pairs) return fail(PA_ERR_INVALID_ARG, "n_pairs is NULL");
+  if (S < 0 || maxb < 0 || cap < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (S > 0 && (!tables || !lens)) return fail(PA_ERR_INVALID_ARG, "NULL tables or lengths");
+  // distinct blocks in order of first appearance, with the group's references
+  std::vector<int32_t> held((size_t)from->P, 0);
+  std::vector<int32_t> order;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t nb = ((int64_t)lens[s] + from->B - 1) / from->B;
+    if (lens[s] < 0 || nb > maxb) return fail(PA_ERR_INVALID_ARG, "length outside the table");
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = tables[(size_t)s * maxb + j];
+      if (!in_range(from, b)) return fail(PA_ERR_INVALID_ARG, "table entry outside the pool");
+      if (held[(size_t)b]++ == 0) order.push_back(b);
+    }
+  }
+  for (int32_t b : order)
+    if (from->ref[(size_t)b] != held[(size_t)b])
+      return fail(PA_ERR_INVALID_ARG, "a block of the group is also mapped outside it");
+  const int32_t n = (int32_t)order.size();
+  if (n > cap || (n > 0 && !pairs)) return fail(PA_ERR_INVALID_ARG, "pairs array too small");
+  if (to->nfree < n) return fail(PA_ERR_OUT_OF_BLOCKS, "destination pool has too few free blocks");
+  // allocate in `to`, in first-appearance order
+  std::vector<int32_t> moved((size_t)from->P, -1);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = order[(size_t)i];
+    const int32_t nb = do_alloc(to);
+    to->ref[(size_t)nb] = held[(size_t)b];
+    moved[(size_t)b] = nb;
+    pairs[2 * i] = b;
+    pairs[2 * i + 1] = nb;
+  }
+  // drop the group's references in `from` (as pa_seq_free, sequence by sequence)
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t nb = (int32_t)(((int64_t)lens[s] + from->B - 1) / from->B);
+    for (int32_t j = 0; j < nb; ++j) do_decref(from, tables[(size_t)s * maxb + j]);
+  }
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t nb = (int32_t)(((int64_t)lens[s] + from->B - 1) / from->B);
+    for (int32_t j = 0; j < nb; ++j) {
+      int32_t& e = tables[(size_t)s * maxb + j];
+      e = moved[(size_t)e];
+    }
+  }
+  *n_pairs = n;
+  return PA_OK;
+}
+
 }  // extern "C"

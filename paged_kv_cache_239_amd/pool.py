@@ -49,9 +49,10 @@ def _ptr(t) -> int:
 class Pool:
     """A paged K/V pool: L layers x (K, V) slabs of P blocks [P][Hkv][B][d].
 
-    ``device`` given: the pool's device memory is a torch uint8 tensor owned
-    by this object.  ``device=None`` builds a manager-only pool (no device
-    memory; device operations are unavailable), used by host-side tests.
+    ``device`` given: the pool's memory is a torch uint8 tensor owned by this
+    object, on that device, or in pinned host memory for ``device="pinned"``
+    (a swap pool).  ``device=None`` builds a manager-only pool (no memory;
+    device operations are unavailable), used by host-side tests.
     """
 
     def __init__(self, L: int, Hkv: int, d: int, B: int, P: int, dtype="f16",
@@ -64,9 +65,21 @@ class Pool:
         if self.nbytes == 0:
             raise _abi.PAError(_abi.PA_ERR_INVALID_ARG, "pa_pool_bytes returned 0 for these sizes")
         self.buffer = None
-        if device is not None:
+        if device == "pinned":
+            # pinned host memory, mapped into the device's address space: a
+            # swap target for pa_swap_blocks
             import torch
-            self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+            self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True)
+            base, nbytes = _ptr(self.buffer), self.nbytes
+        elif device is not None:
+            import torch
+            if str(device) == "cpu":
+                # plain host memory carries no alignment promise: over-allocate
+                raw = torch.empty(self.nbytes + 256, dtype=torch.uint8)
+                off = (-_ptr(raw)) % 256
+                self.buffer = raw[off: off + self.nbytes]
+            else:
+                self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
             base, nbytes = _ptr(self.buffer), self.nbytes
         else:
             base, nbytes = 256, self.nbytes   # stand-in address, never dereferenced
@@ -200,6 +213,20 @@ class Pool:
                                                 _i32p(out), _i32p(out_lens)))
         return out[:S_new], out_lens[:S_new]
 
+    def move_blocks(self, to: "Pool", tables: np.ndarray, lens) -> np.ndarray:
+        """Swap a group of sequences from this pool to ``to`` (host manager):
+        ``tables`` (int32 [S][maxb]) are rewritten in place to name blocks of
+        ``to``.  Returns the (old, new) block pairs, int32 [N][2]."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
+        S, maxb = tables.shape
+        ln = _as_i32(lens)
+        cap = int(S * maxb)
+        pairs = np.zeros((max(cap, 1), 2), dtype=np.int32)
+        n = C.c_int32()
+        check(self.lib, self.lib.pa_move_blocks(self.handle, to.handle, _i32p(tables), _i32p(ln), S, maxb,
+                                                _i32p(pairs), cap, C.byref(n)))
+        return pairs[: n.value].copy()
+
     # ---- device operations -------------------------------------------------------
     def write_kv(self, layer: int, k, v, slot_mapping, stream=None) -> None:
         """k, v: device [S][Hkv][d] of the pool dtype; slot_mapping: device int64 [S]."""
@@ -213,6 +240,13 @@ class Pool:
         if N == 0:
             return
         check(self.lib, self.lib.pa_copy_blocks(self.handle, _ptr(pairs), N, _stream_handle(stream)))
+
+    def swap_blocks(self, to: "Pool", pairs, stream=None) -> None:
+        """pairs: device int32 [N][2] (block of this pool, block of ``to``)."""
+        N = int(pairs.shape[0])
+        if N == 0:
+            return
+        check(self.lib, self.lib.pa_swap_blocks(self.handle, to.handle, _ptr(pairs), N, _stream_handle(stream)))
 
     def workspace_bytes(self, S: int, Hq: int, max_ctx: int) -> int:
         return int(self.lib.pa_decode_workspace_bytes(self.handle, S, Hq, max_ctx))
