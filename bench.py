@@ -144,6 +144,9 @@ def main() -> int:
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="instead of decode steps: swap the first N sequences of the workload out to a "
                          "pinned host pool and back, and time it")
+    ap.add_argument("--queries", type=int, default=0, metavar="Q",
+                    help="instead of one token per sequence: every step appends Q tokens per sequence "
+                         "(speculative verification, chunked prefill) and runs multi-query attention")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
@@ -180,6 +183,8 @@ def main() -> int:
 
     if args.swap:
         return swap_bench(args)
+    if args.queries:
+        return multi_query_bench(args)
 
     W, K = args.warmup, args.steps
     wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
@@ -403,6 +408,128 @@ def main() -> int:
     if args.cpu_baseline == "on":
         result["cpu_baseline"], result["parity"] = cpu_baseline(wl, eng, snaps, outs, W + K, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def multi_query_bench(args) -> int:
+    """Q new tokens per sequence per step: the host manager reserves their
+    slots, pa_write_kv stores their keys/values, and every layer runs
+    pa_multi_query_attention (query t of a sequence attends causally up to
+    its own position).  Algorithmic bytes per layer: every useful key/value
+    position once, the queries and outputs, the tables; flops per layer:
+    4 d per (query head, visible position)."""
+    import torch
+
+    from paged_kv_cache_239_amd import multi_query_workspace
+    from paged_kv_cache_239_amd.engine import DecodeEngine
+    from workloads import make_workload, with_headroom
+
+    Q, W, K = args.queries, args.warmup, args.steps
+    wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), (W + K) * Q + 1)
+    c = wl.cfg
+    maxb = wl.max_blocks((W + K) * Q + 1)
+    eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, maxb, free_order=wl.free_order)
+    for layer in range(c.L):
+        for which in ("k", "v"):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(wl.pool_fill_seed(layer, which))
+            eng.pool.slab(layer, which).normal_(generator=g)
+    for op in wl.history:
+        if op[0] == "append":
+            eng.append(op[1], op[2])
+        else:
+            eng.fork(op[1], op[2], op[3])
+    T = wl.S * Q
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.pool_fill_seed(0, "k") ^ 0x5A5A)
+    qs = [torch.randn((T, c.Hq, c.d), generator=gen, device="cuda").to(tdt) for _ in range(c.L)]
+    kn = [torch.randn((T, c.Hkv, c.d), generator=gen, device="cuda").to(tdt) for _ in range(c.L)]
+    vn = [torch.randn((T, c.Hkv, c.d), generator=gen, device="cuda").to(tdt) for _ in range(c.L)]
+    outs = [torch.empty_like(x) for x in qs]
+    q_start = torch.arange(0, T + 1, Q, dtype=torch.int32, device="cuda")
+    scale = float(wl.scale)
+    ws = multi_query_workspace(eng.pool, wl.S, c.Hq, maxb * c.B, Q)
+    d_slots = torch.empty(T, dtype=torch.int64, device="cuda")
+
+    def step(events=None):
+        slots = np.empty(T, dtype=np.int64)
+        pairs = []
+        for s in range(wl.S):
+            sl, pr = eng.append(s, Q)
+            slots[s * Q:(s + 1) * Q] = sl
+            pairs += pr
+        eng.upload_tables()
+        d_slots.copy_(torch.from_numpy(slots))
+        if pairs:
+            eng.pool.copy_blocks(torch.tensor(pairs, dtype=torch.int32, device="cuda"))
+        max_ctx = int(eng.lens.max())
+        for layer in range(c.L):
+            eng.pool.write_kv(layer, kn[layer], vn[layer], d_slots)
+            if events is not None and layer == events[2]:
+                events[0].record()
+            eng.pool.multi_query_attention(layer, outs[layer], qs[layer], q_start, eng.d_tables, eng.d_lens,
+                                           max_ctx, Q, scale, workspace=ws)
+            if events is not None and layer == events[2]:
+                events[1].record()
+        return eng.lens.copy()
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    att = []
+    lens_hist = []
+    t_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    e0.record()
+    for i in range(K):
+        lens_hist.append(step((t_ev[i][0], t_ev[i][1], (7 * i) % c.L)))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    att_us = float(np.mean([a.elapsed_time(b) for a, b in t_ev])) * 1e3
+
+    def layer_bytes(lens):
+        lens = np.asarray(lens, dtype=np.int64)
+        return (int(lens.sum()) * 2 * c.Hkv * c.d * 2 + 2 * T * c.Hq * c.d * 2
+                + int(np.sum(-(-lens // c.B))) * 4 + wl.S * 8)
+
+    def layer_flops(lens):
+        # query t of nq sees n - nq + t + 1 positions; 4 d flops per (head, position)
+        vis = sum(int(n) * Q - Q * (Q - 1) // 2 for n in lens)
+        return 4 * c.d * c.Hq * vis
+
+    ab = float(np.mean([layer_bytes(x) for x in lens_hist]))
+    fl = float(np.mean([layer_flops(x) for x in lens_hist]))
+    wbytes = 2 * (2 * T * c.Hkv * c.d * 2) + 8 * T
+    step_bytes = c.L * (ab + wbytes)
+    gbs = ab / (att_us * 1e-6) / 1e9
+    tfs = fl / (att_us * 1e-6) / 1e12
+    hbm = gbs / HBM_PEAK_GBS
+    alu = tfs / 157.3
+    res = {
+        "metric": "multi-query paged attention: achieved HBM GB/s and TFLOP/s + query tokens/s",
+        "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": f"{c.name}: every step appends {Q} tokens to each of {wl.S} sequences "
+                               f"(context {int(wl.lengths0.min()) - 1}..{int(wl.lengths0.max()) - 1} before the first step)",
+                   "queries_per_sequence": Q, "block_size": c.B, "layers": c.L},
+        "query_tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"kernel": f"decode_attention_kernel<{c.dtype},rows=8,B={c.B},QT={8 // c.G}> + merge",
+                     "bound": "hbm" if hbm >= alu else "alu",
+                     "achieved": round(gbs, 1) if hbm >= alu else round(tfs, 2),
+                     "peak": HBM_PEAK_GBS if hbm >= alu else 157.3,
+                     "unit": "GB/s" if hbm >= alu else "TFLOP/s",
+                     "frac": round(max(hbm, alu), 4),
+                     "hbm_gbs": round(gbs, 1), "tflops": round(tfs, 2),
+                     "alg_bytes_per_launch": int(ab), "flops_per_launch": int(fl),
+                     "avg_launch_us": round(att_us, 2),
+                     "note": "alu peak = fp32 vector 157.3 TFLOP/s; the query-key products use packed "
+                             "16-bit dot instructions"},
+    }
+    print(json.dumps(res), flush=True)
     return 0
 
 

@@ -316,6 +316,39 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k,
                                        float scale, void* workspace,
                                        size_t ws_bytes, hipStream_t stream);
 
+/* Several query tokens per sequence over the same block tables: chunked
+ * prefill ("vLLM PagedAttention and continuous batching", section "Chunked
+ * prefill": a prefill that does not fit the step's budget is split, each
+ * chunk attending to the cache written so far) and speculative verification
+ * ("PagedAttention and Online Inference", section 5: speculative decoding
+ * creates several new positions at once).  Sequence s has queries
+ * q_start[s] .. q_start[s+1]-1 (nq of them) for its last nq positions,
+ * whose keys and values are already in the cache (pa_write_kv): query t
+ * sits at position n - nq + t, n = context_lens[s], and attends to
+ * positions 0 .. n - nq + t (causal inside the new tokens).
+ *   q, out      : device [T][Hq][d], row q_start[s] + t for query t of s
+ *   q_start     : device int32 [S+1], nondecreasing, q_start[S] <= T; the
+ *                 kernel clamps every entry into [0, T]
+ *   max_q       : an upper bound of every nq (queries beyond it are not
+ *                 computed); nq must not exceed context_lens[s]
+ *   workspace   : >= pa_multi_query_workspace_bytes(pool, S, Hq, max_ctx,
+ *                 max_q) bytes, 256-byte aligned, or NULL when that is 0
+ * Other arguments, supported shapes and errors as pa_decode_attention; with
+ * q_start[s+1] - q_start[s] = 1 for every s the result equals it. */
+pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out,
+                                   const void* q, const int32_t* q_start, int T,
+                                   int S, int Hq, const int32_t* block_tables,
+                                   int maxb, const int32_t* context_lens,
+                                   int max_ctx, int max_q, float scale,
+                                   void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Workspace bytes for pa_multi_query_attention up to these sizes (never
+ * decreasing in any argument); 0 if none is needed or the shape is
+ * unsupported. */
+size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq,
+                                      int max_ctx, int max_q);
+
 /* Message describing the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);
 

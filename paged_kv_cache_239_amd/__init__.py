@@ -7,6 +7,7 @@ streams.
 """
 
 from ._abi import OutOfBlocks, PAError, PA_BF16, PA_F16  # noqa: F401
-from .pool import Pool, decode_workspace, dtype_code  # noqa: F401
+from .pool import Pool, decode_workspace, dtype_code, multi_query_workspace  # noqa: F401
 
-__all__ = ["Pool", "PAError", "OutOfBlocks", "decode_workspace", "dtype_code", "PA_F16", "PA_BF16"]
+__all__ = ["Pool", "PAError", "OutOfBlocks", "decode_workspace", "multi_query_workspace", "dtype_code", "PA_F16",
+           "PA_BF16"]

@@ -219,12 +219,15 @@ struct DecodeArgs {
   const char* kslab;        // layer's key slab   [P][Hkv][B][d]
   const char* vslab;        // layer's value slab [P][Hkv][B][d]
   uint64_t tile_bytes;      // Hkv * B * d * 2: stride of one physical block
-  const uint16_t* q;        // [S][Hq][d]
-  uint16_t* out;            // [S][Hq][d]
+  const uint16_t* q;        // [S][Hq][d]; several queries per sequence: [T][Hq][d]
+  uint16_t* out;            // same shape as q
   const int32_t* tables;    // [S][maxb]
   const int32_t* lens;      // [S]
-  float* ws_ml;             // [S][Hkv][nparts_max][G][2]  (max, normaliser)
-  float* ws_acc;            // [S][Hkv][nparts_max][G][d]
+  float* ws_ml;             // [S][ntiles][Hkv][nparts_max][G][2]  (max, normaliser)
+  float* ws_acc;            // [S][ntiles][Hkv][nparts_max][G][d]
+  const int32_t* q_start;   // [S+1] first query row of each sequence (several queries), or null
+  int ntiles;               // query tiles per sequence (1 for single-query decode)
+  int T;                    // query rows in q and out (several queries; row indices are clamped to it)
   const uint4* knew;        // [S][Hkv][d] this step's keys (fused cache write) or null
   const uint4* vnew;        // [S][Hkv][d] this step's values, or null
   const int64_t* slots;     // [S] their slots, or null
@@ -241,9 +244,16 @@ struct DecodeArgs {
 #define PA_OCCUPANCY
 #endif
 
-template <bool BF16, int G, int BS, int NW>
+// QT = 0: one query token per sequence (decode); the G rows are the query
+// heads of one key/value head.  QT > 0: several query tokens per sequence
+// at its last positions, each attending causally (up to its own position);
+// a workgroup takes QT of them, and its G rows are (token t, head g) =
+// (row / GQ, row % GQ) with GQ = G / QT query heads per key/value head.
+template <bool BF16, int G, int BS, int NW, int QT>
 __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a) {
   using SC = Scores<G>;
+  constexpr int GQ = QT > 0 ? G / QT : G;
+  static_assert(QT == 0 || GQ * QT == G, "rows = query tokens x query heads");
   constexpr int E = SC::E;
   // A 16-token step lies inside one block when 16 | BS; with 8-token blocks
   // it covers two (loads 0-1 read the first, loads 2-3 the second).
@@ -256,10 +266,17 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   //            of every sequence for every XCD;
   //   order 1: partition fastest with an odd partition stride, so the
   //            partitions of one (sequence, head) spread over all XCDs.
-  int kvh, s, p;
+  int kvh, s, p, tile = 0;
   {
     const uint32_t id = blockIdx.x;
-    if (a.grid_order == 0) {
+    if (QT > 0) {                      // head, then query tile, sequence, partition
+      kvh = id % a.Hkv;
+      uint32_t t = id / a.Hkv;
+      tile = t % a.ntiles;
+      t /= a.ntiles;
+      s = t % a.S;
+      p = t / a.S;
+    } else if (a.grid_order == 0) {
       kvh = id % a.Hkv;
       const uint32_t t = id / a.Hkv;
       s = t % a.S;
@@ -282,9 +299,21 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   const int t_begin = p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
   const int32_t* table = a.tables + (size_t)s * a.maxb;
-  const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
   uint4 qv = make_uint4(0, 0, 0, 0);
-  if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
+  int q0 = 0, nq = 1;   // several queries: first row of the sequence, its query count
+  if constexpr (QT == 0) {
+    const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)s * a.Hq + (size_t)kvh * G) * kD);
+    if (threadIdx.x < G * 16) qv = qg[threadIdx.x];
+  } else {
+    // row offsets are clamped into [0, T] so that q and out stay in bounds
+    q0 = min(max(a.q_start[s], 0), a.T);
+    nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
+    const int row = threadIdx.x >> 4;
+    const int tq = tile * QT + row / GQ;
+    if (threadIdx.x < G * 16 && tq < nq)
+      qv = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + row % GQ) * kD)[threadIdx.x & 15];
+  }
   int entry[BPG];
 #pragma unroll
   for (int b = 0; b < BPG; ++b) {
@@ -294,6 +323,16 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
 
   int n = a.lens[s];
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  // Several queries: query t of the sequence sits at position n - nq + t and
+  // sees positions 0 .. n - nq + t.  This tile's rows see at least lim_min
+  // and at most n (now the tile's context) positions.
+  int lim_min = n;
+  if constexpr (QT > 0) {
+    nq = __builtin_amdgcn_readfirstlane(nq);
+    if (tile * QT >= nq || nq > n) return;
+    lim_min = n - nq + tile * QT + 1;
+    n = n - nq + min(tile * QT + QT, nq);
+  }
   n = __builtin_amdgcn_readfirstlane(n);
   const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
   if (p >= nparts) return;
@@ -327,7 +366,8 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   // groups of 16 tokens in this partition, dealt round-robin to the waves:
   // the k-th group of this wave is g_first + k * NW, and lane k holds that
   // group's physical block (one lane read per group later).
-  int g_full = t_end / 16;                     // groups [.., g_full) are full
+  // groups [.., g_full) are full and seen whole by every row
+  int g_full = (QT > 0 ? min(t_end, lim_min) : t_end) / 16;
   const int g_last = (t_end + 15) / 16;        // a tail group exists if g_full < g_last
   uint4 qr[G];
   int my_phys[BPG];
@@ -346,7 +386,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   // which coarsens every wait on the prefetched loads.)
   int g_new = -1, j_new = 0, r_new = 0;
   uint4 k_reg = make_uint4(0, 0, 0, 0), v_reg = make_uint4(0, 0, 0, 0);
-  if (a.slots != nullptr && p == nparts - 1) {
+  if (QT == 0 && a.slots != nullptr && p == nparts - 1) {
     const int64_t slot = a.slots[s];
     if (slot >= 0 && slot < a.nslots) {
       const size_t src = ((size_t)s * a.Hkv + kvh) * 16 + c;
@@ -440,7 +480,9 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
       sc[e] = x[e] * a.scale_log2;
       if (tail) {
         const int j = SC::value_index(c, e) & 3;
-        if (tok0 + 4 * j + r >= n) sc[e] = -INFINITY;
+        // row (t, g) sees positions below lim_min + t (QT > 0), all rows below n (QT = 0)
+        const int lim = QT > 0 ? lim_min + (SC::value_index(c, e) >> 2) / GQ : n;
+        if (tok0 + 4 * j + r >= lim) sc[e] = -INFINITY;
       }
       mx = fmaxf(mx, sc[e]);
     }
@@ -531,10 +573,19 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
         process_group(g_first + k * NW, K0, V0, false);
       }
     }
-    if (g_full < g_last && g_full >= g_first && (g_full - g_first) % NW == 0) {
-      const int kt = (g_full - g_first) / NW;
-      load_group(kt, K0, V0, true);
-      process_group(g_full, K0, V0, true);
+    if constexpr (QT == 0) {
+      if (g_full < g_last && g_full >= g_first && (g_full - g_first) % NW == 0) {
+        const int kt = (g_full - g_first) / NW;
+        load_group(kt, K0, V0, true);
+        process_group(g_full, K0, V0, true);
+      }
+    } else {
+      // the steps where some rows stop (the causal edge), with per-row masks
+      int g = g_full > g_first ? g_first + (g_full - g_first + NW - 1) / NW * NW : g_first;
+      for (; g < g_last; g += NW) {
+        load_group((g - g_first) / NW, K0, V0, true);
+        process_group(g, K0, V0, true);
+      }
     }
   }
 
@@ -602,9 +653,16 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     }
   }
 
-  uint4* out_row = reinterpret_cast<uint4*>(a.out + ((size_t)s * a.Hq + (size_t)kvh * G + wh) * kD) + wc;
+  size_t orow = (size_t)s * a.Hq + (size_t)kvh * G + wh;
+  bool live = worker;
+  if constexpr (QT > 0) {
+    const int tq = tile * QT + wh / GQ;
+    orow = (size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + wh % GQ;
+    live = worker && tq < nq;
+  }
+  uint4* out_row = reinterpret_cast<uint4*>(a.out + orow * kD) + wc;
   if (nparts == 1) {
-    if (worker) {
+    if (live) {
       const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
       float o[8];
 #pragma unroll
@@ -616,7 +674,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
 
   // ---- several partitions: store this partition's (m, l, acc) --------------
   if (worker) {
-    const size_t pbase = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
+    const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
     float4* dst = reinterpret_cast<float4*>(a.ws_acc + ((pbase + p) * G + wh) * kD + 8 * wc);
     dst[0] = make_float4(A[0], A[1], A[2], A[3]);
     dst[1] = make_float4(A[4], A[5], A[6], A[7]);
@@ -628,13 +686,15 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
 // merge of the context partitions (eq. (4) rescale): one wave per
 // (sequence, key/value head); thread = (head, 8-dim chunk)
 // ---------------------------------------------------------------------------
-template <bool BF16, int G>
+template <bool BF16, int G, int QT>
 __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a) {
+  constexpr int GQ = QT > 0 ? G / QT : G;
   const int kvh = blockIdx.x;
   const int s = blockIdx.y;
+  const int tile = QT > 0 ? (int)blockIdx.z : 0;
   const int wh = threadIdx.x >> 4;
   const int wc = threadIdx.x & 15;
-  const size_t pbase = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
+  const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
   // Partitions are read CHUNK at a time with all loads of a chunk in flight;
   // the first chunk is requested together with the context length (its
   // indices are clamped into the workspace; unused entries are ignored).
@@ -654,6 +714,17 @@ __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a
   fetch(0);
   int n = a.lens[s];
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  size_t orow = (size_t)s * a.Hq + (size_t)kvh * G + wh;
+  if constexpr (QT > 0) {
+    // the same tile context and rows as the partition kernel
+    const int q0 = min(max(a.q_start[s], 0), a.T);
+    const int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
+    if (tile * QT >= nq || nq > n) return;
+    n = n - nq + min(tile * QT + QT, nq);
+    const int tq = tile * QT + wh / GQ;
+    if (tq >= nq) return;
+    orow = (size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + wh % GQ;
+  }
   const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
   if (nparts <= 1) return;  // written directly by the partition kernel
   float Mg = -INFINITY, Lg = 0.0f, Ag[8];
@@ -683,7 +754,7 @@ __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = Ag[i] * inv;
-  uint4* out_row = reinterpret_cast<uint4*>(a.out + ((size_t)s * a.Hq + (size_t)kvh * G + wh) * kD) + wc;
+  uint4* out_row = reinterpret_cast<uint4*>(a.out + orow * kD) + wc;
   *out_row = narrow8<BF16>(o);
 }
 
@@ -745,32 +816,49 @@ WsLayout ws_layout(int S, int Hkv, int G, const LaunchCfg& cfg) {
   return w;
 }
 
-template <bool BF16, int G, int BS>
+template <bool BF16, int G, int BS, int QT>
 void launch_decode(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves, QT>), grid, dim3(kWaves * 64), 0, stream, args);
   if (args.nparts_max > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, G>), dim3(args.Hkv, args.S), dim3(G * 16), 0, stream, args);
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, G, QT>), dim3(args.Hkv, args.S, args.ntiles), dim3(G * 16), 0,
+                       stream, args);
 }
 
+// G query heads per key/value head.  One query per sequence: the rows of a
+// workgroup are those G heads.  Several: 8 rows = 8 / G query tokens x G heads.
 template <bool BF16, int BS>
-bool dispatch_g(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+bool dispatch_g(int G, bool multi, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  if (multi) {
+    switch (G) {
+      case 1: launch_decode<BF16, 8, BS, 8>(args, grid, stream); return true;
+      case 2: launch_decode<BF16, 8, BS, 4>(args, grid, stream); return true;
+      case 4: launch_decode<BF16, 8, BS, 2>(args, grid, stream); return true;
+      case 8: launch_decode<BF16, 8, BS, 1>(args, grid, stream); return true;
+      default: return false;
+    }
+  }
   switch (G) {
-    case 1: launch_decode<BF16, 1, BS>(args, grid, stream); return true;
-    case 2: launch_decode<BF16, 2, BS>(args, grid, stream); return true;
-    case 4: launch_decode<BF16, 4, BS>(args, grid, stream); return true;
-    case 8: launch_decode<BF16, 8, BS>(args, grid, stream); return true;
+    case 1: launch_decode<BF16, 1, BS, 0>(args, grid, stream); return true;
+    case 2: launch_decode<BF16, 2, BS, 0>(args, grid, stream); return true;
+    case 4: launch_decode<BF16, 4, BS, 0>(args, grid, stream); return true;
+    case 8: launch_decode<BF16, 8, BS, 0>(args, grid, stream); return true;
     default: return false;
   }
 }
+
+// query tokens per workgroup when a sequence has several queries
+int tile_tokens(int G) { return 8 / G; }
 
 }  // namespace
 
 namespace {
 
+// q_start == nullptr: one query per sequence (decode).  Otherwise sequence s
+// has queries q_start[s] .. q_start[s+1]-1 of T rows, at most max_q of them.
 pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int S, int Hq,
                         const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx, float scale,
                         void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
-                        const int64_t* slot_mapping, hipStream_t stream) {
+                        const int64_t* slot_mapping, const int32_t* q_start, int T, int max_q, hipStream_t stream) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
   if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
@@ -789,9 +877,19 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
+  const bool multi = q_start != nullptr;
+  int ntiles = 1;
+  if (multi) {
+    if (!aligned(q_start, 4)) return fail(PA_ERR_INVALID_ARG, "q_start must be 4-byte aligned");
+    if (T < 0 || max_q < 0) return fail(PA_ERR_INVALID_ARG, "negative T or max_q");
+    if (T == 0 || max_q == 0) return PA_OK;
+    ntiles = (max_q + tile_tokens(G) - 1) / tile_tokens(G);
+    if (ntiles > 65535) return fail(PA_ERR_UNSUPPORTED, "max_q too large");
+  }
+  const int rows = multi ? 8 : G;
 
-  const LaunchCfg cfg = choose_launch(S, pool->Hkv, max_ctx);
-  const WsLayout wl = ws_layout(S, pool->Hkv, G, cfg);
+  const LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx);
+  const WsLayout wl = ws_layout(S * ntiles, pool->Hkv, rows, cfg);
   char* ws = static_cast<char*>(workspace);
   if (wl.total > 0) {
     if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
@@ -821,21 +919,24 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   args.vnew = static_cast<const uint4*>(v_new);
   args.slots = slot_mapping;
   args.nslots = (int64_t)pool->P * pool->B;
+  args.q_start = q_start;
+  args.ntiles = ntiles;
+  args.T = T;
 
   static const int grid_order = env_int("PA_GRID_ORDER", 0) == 1 ? 1 : 0;
   args.grid_order = grid_order;
   args.pstride = cfg.nparts_max | 1;
-  const uint64_t nwg = (uint64_t)pool->Hkv * S * (grid_order == 0 ? cfg.nparts_max : args.pstride);
+  const uint64_t nwg = (uint64_t)pool->Hkv * S * ntiles * (grid_order == 0 || multi ? cfg.nparts_max : args.pstride);
   if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
   switch (pool->B) {
-    case 8: ok = bf16 ? dispatch_g<true, 8>(G, args, grid, stream) : dispatch_g<false, 8>(G, args, grid, stream); break;
-    case 16: ok = bf16 ? dispatch_g<true, 16>(G, args, grid, stream) : dispatch_g<false, 16>(G, args, grid, stream); break;
-    case 32: ok = bf16 ? dispatch_g<true, 32>(G, args, grid, stream) : dispatch_g<false, 32>(G, args, grid, stream); break;
-    case 64: ok = bf16 ? dispatch_g<true, 64>(G, args, grid, stream) : dispatch_g<false, 64>(G, args, grid, stream); break;
-    default: ok = bf16 ? dispatch_g<true, 128>(G, args, grid, stream) : dispatch_g<false, 128>(G, args, grid, stream); break;
+    case 8: ok = bf16 ? dispatch_g<true, 8>(G, multi, args, grid, stream) : dispatch_g<false, 8>(G, multi, args, grid, stream); break;
+    case 16: ok = bf16 ? dispatch_g<true, 16>(G, multi, args, grid, stream) : dispatch_g<false, 16>(G, multi, args, grid, stream); break;
+    case 32: ok = bf16 ? dispatch_g<true, 32>(G, multi, args, grid, stream) : dispatch_g<false, 32>(G, multi, args, grid, stream); break;
+    case 64: ok = bf16 ? dispatch_g<true, 64>(G, multi, args, grid, stream) : dispatch_g<false, 64>(G, multi, args, grid, stream); break;
+    default: ok = bf16 ? dispatch_g<true, 128>(G, multi, args, grid, stream) : dispatch_g<false, 128>(G, multi, args, grid, stream); break;
   }
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
   return hip_check(hipGetLastError(), "decode attention launch");
@@ -876,7 +977,32 @@ pa_status pa_decode_attention(pa_pool* pool, int layer, void* out, const void* q
                               float scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
   pa_detail::clear_error();
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
-                       ws_bytes, nullptr, nullptr, nullptr, stream);
+                       ws_bytes, nullptr, nullptr, nullptr, nullptr, 0, 0, stream);
+}
+
+size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx, int max_q) {
+  if (!pool || S <= 0 || Hq <= 0 || max_ctx < 0 || max_q <= 0 || Hq % pool->Hkv) return 0;
+  const int G = Hq / pool->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
+  const int64_t ntiles = (max_q + tile_tokens(G) - 1) / tile_tokens(G);
+  if (ntiles * S > 0x7fffffff) return 0;
+  // as pa_decode_workspace_bytes: the shortest partition, so the size never
+  // decreases with any argument
+  LaunchCfg cfg;
+  cfg.part_tokens = 16 * kWaves;
+  cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
+  if (cfg.nparts_max <= 1 && max_ctx > 0) cfg.nparts_max = 2;
+  return ws_layout((int)(S * ntiles), pool->Hkv, 8, cfg).total;
+}
+
+pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out, const void* q, const int32_t* q_start, int T,
+                                   int S, int Hq, const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                   int max_ctx, int max_q, float scale, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  pa_detail::clear_error();
+  if (S > 0 && !q_start) return fail(PA_ERR_INVALID_ARG, "NULL q_start");
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
+                       ws_bytes, nullptr, nullptr, nullptr, q_start, T, max_q, stream);
 }
 
 pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, const void* v,
@@ -891,7 +1017,7 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, 
       return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
   }
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
-                       ws_bytes, k, v, slot_mapping, stream);
+                       ws_bytes, k, v, slot_mapping, nullptr, 0, 0, stream);
 }
 
 }  // extern "C"

@@ -264,6 +264,20 @@ class Pool:
             int(max_ctx), C.c_float(scale), C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes),
             _stream_handle(stream)))
 
+    def multi_query_attention(self, layer: int, out, q, q_start, block_tables, context_lens, max_ctx: int,
+                              max_q: int, scale: float, workspace=None, stream=None) -> None:
+        """out, q: device [T][Hq][d]; q_start: device int32 [S+1] (queries of
+        sequence s are rows q_start[s] .. q_start[s+1]-1, its last positions);
+        block_tables: device int32 [S][maxb]; context_lens: device int32 [S]."""
+        T, Hq = int(q.shape[0]), int(q.shape[1])
+        S = int(q_start.shape[0]) - 1
+        maxb = int(block_tables.shape[1])
+        ws_ptr, ws_bytes = (0, 0) if workspace is None else (_ptr(workspace), int(workspace.numel()))
+        check(self.lib, self.lib.pa_multi_query_attention(
+            self.handle, layer, _ptr(out), _ptr(q), _ptr(q_start), T, S, Hq, _ptr(block_tables), maxb,
+            _ptr(context_lens), int(max_ctx), int(max_q), C.c_float(scale), C.c_void_p(ws_ptr or None),
+            C.c_size_t(ws_bytes), _stream_handle(stream)))
+
     def write_kv_decode_attention(self, layer: int, k, v, slot_mapping, out, q, block_tables, context_lens,
                                   max_ctx: int, scale: float, workspace=None, stream=None) -> None:
         """write_kv then decode_attention for one layer in one pass (see
@@ -275,6 +289,17 @@ class Pool:
             self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(out), _ptr(q), S, Hq,
             _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), C.c_float(scale),
             C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
+
+
+def multi_query_workspace(pool: Pool, S: int, Hq: int, max_ctx: int, max_q: int, device="cuda", stream=None):
+    """A zero-initialised workspace for ``pool.multi_query_attention``."""
+    import torch
+    nbytes = int(pool.lib.pa_multi_query_workspace_bytes(pool.handle, S, Hq, max_ctx, max_q))
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    check(pool.lib, pool.lib.pa_decode_workspace_init(_ptr(ws), nbytes, _stream_handle(stream)))
+    return ws
 
 
 def decode_workspace(pool: Pool, S: int, Hq: int, max_ctx: int, device="cuda", stream=None):
