@@ -505,8 +505,14 @@ def multi_query_bench(args) -> int:
     step_bytes = c.L * (ab + wbytes)
     gbs = ab / (att_us * 1e-6) / 1e9
     tfs = fl / (att_us * 1e-6) / 1e12
+    # more than 8 rows (query tokens x heads) per sequence run on the matrix
+    # cores (dense 16-bit MFMA peak), fewer on the fp32 vector units
+    mfma = Q * c.G > 8
+    cpeak = 2500.0 if mfma else 157.3
+    ridge = cpeak * 1e12 / (HBM_PEAK_GBS * 1e9)          # flop per byte where the roofs meet
+    mem_bound = fl / ab < ridge
     hbm = gbs / HBM_PEAK_GBS
-    alu = tfs / 157.3
+    alu = tfs / cpeak
     res = {
         "metric": "multi-query paged attention: achieved HBM GB/s and TFLOP/s + query tokens/s",
         "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
@@ -517,17 +523,21 @@ def multi_query_bench(args) -> int:
                                f"(context {int(wl.lengths0.min()) - 1}..{int(wl.lengths0.max()) - 1} before the first step)",
                    "queries_per_sequence": Q, "block_size": c.B, "layers": c.L},
         "query_tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": f"decode_attention_kernel<{c.dtype},rows=8,B={c.B},QT={8 // c.G}> + merge",
-                     "bound": "hbm" if hbm >= alu else "alu",
-                     "achieved": round(gbs, 1) if hbm >= alu else round(tfs, 2),
-                     "peak": HBM_PEAK_GBS if hbm >= alu else 157.3,
-                     "unit": "GB/s" if hbm >= alu else "TFLOP/s",
-                     "frac": round(max(hbm, alu), 4),
+        "roofline": {"kernel": (f"mq_mfma_kernel<{c.dtype},G={c.G},B={c.B}> + merge" if mfma else
+                                f"decode_attention_kernel<{c.dtype},rows=8,B={c.B},QT={8 // c.G}> + merge"),
+                     "bound": "hbm" if mem_bound else ("mfma" if mfma else "alu"),
+                     "achieved": round(gbs, 1) if mem_bound else round(tfs, 2),
+                     "peak": HBM_PEAK_GBS if mem_bound else cpeak,
+                     "unit": "GB/s" if mem_bound else "TFLOP/s",
+                     "frac": round(hbm if mem_bound else alu, 4),
                      "hbm_gbs": round(gbs, 1), "tflops": round(tfs, 2),
+                     "compute_peak_tflops": cpeak,
+                     "intensity_flop_per_byte": round(fl / ab, 1), "ridge_flop_per_byte": round(ridge, 1),
                      "alg_bytes_per_launch": int(ab), "flops_per_launch": int(fl),
                      "avg_launch_us": round(att_us, 2),
-                     "note": "alu peak = fp32 vector 157.3 TFLOP/s; the query-key products use packed "
-                             "16-bit dot instructions"},
+                     "note": "bound from the arithmetic intensity of the algorithmic bytes and flops against "
+                             "the ridge point; compute peak: dense 16-bit MFMA 2.5 PFLOP/s on the matrix path, "
+                             "fp32 vector 157.3 TFLOP/s on the vector path"},
     }
     print(json.dumps(res), flush=True)
     return 0

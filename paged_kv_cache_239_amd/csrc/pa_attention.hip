@@ -758,6 +758,311 @@ __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a
   *out_row = narrow8<BF16>(o);
 }
 
+// ---------------------------------------------------------------------------
+// several queries per sequence on the matrix cores
+//
+// A workgroup's 16 rows are QT = 16 / GQ query tokens x GQ query heads of one
+// key/value head.  Lane = (row = lane % 16, quarter kq = lane / 16).  Per
+// 16-token step of a wave:
+//   S^T[token][row] = K[token][:] . Q[row][:]   4 x mfma 16x16x32: A = the
+//       key tile as loaded (lane: token `row`, dims 32ks + 8kq .. +7), B = Q^T
+//       held in registers (lane: query row `row`, the same dims); the result
+//       gives lane (row, kq) the scores of tokens 4kq .. 4kq+3 for its row;
+//   O^T[dim][row] += V^T[dim][token] . P^T[token][row]   8 x mfma 16x16x16:
+//       B = the lane's own four probabilities (the layout S^T came out in),
+//       A = V^T, read from a per-wave LDS copy of the value tile (token t
+//       stored at row (t % 4) * 4 + t / 4, 288-byte stride: the four quarters
+//       of a wave hit disjoint banks); lane (row, kq) accumulates dims
+//       16nb + 4kq .. +3 of its row, so the softmax state of a row and its
+//       rescale stay inside the lane.
+// Probabilities enter the P.V products in the storage type (the products
+// accumulate in fp32); for bf16 as a rounded part plus the rounded remainder.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma_k32(const uint4 a, const uint4 b, f32x4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma_k16(const uint2 a, const uint2 b, f32x4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c,
+                                                     0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                 0, 0);
+}
+
+constexpr int kVRow = 288;   // bytes per token row of the LDS value tile (256 + 32 pad)
+
+template <bool BF16, int GQ, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
+  constexpr int R = 16;             // rows per workgroup
+  constexpr int QT = R / GQ;        // query tokens per workgroup
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
+  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;
+
+  int kvh, s, p, tile;
+  {
+    const uint32_t id = blockIdx.x;   // head, then query tile, sequence, partition
+    kvh = id % a.Hkv;
+    uint32_t t = id / a.Hkv;
+    tile = t % a.ntiles;
+    t /= a.ntiles;
+    s = t % a.S;
+    p = t / a.S;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15;
+  const int kq = lane >> 4;
+
+  const int t_begin = p * a.part_tokens;
+  const int g_first = t_begin / 16 + wave;
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  int entry[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    const int idx = ((g_first + lane * NW) * 16) / BS + b;
+    entry[b] = table[idx < a.maxb ? idx : a.maxb - 1];
+  }
+  const int q0 = min(max(a.q_start[s], 0), a.T);
+  int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
+  const int tq = tile * QT + row / GQ;    // this lane's query token
+  uint4 qb[4];
+  {
+    const bool live = tq < nq;
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        a.q + ((size_t)(live ? q0 + tq : 0) * a.Hq + (size_t)kvh * GQ + row % GQ) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
+  }
+
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  nq = __builtin_amdgcn_readfirstlane(nq);
+  if (tile * QT >= nq || nq > n) return;
+  const int lim_min = n - nq + tile * QT + 1;
+  n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
+  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
+  if (p >= nparts) return;
+  const int t_end = min(n, t_begin + a.part_tokens);
+  const int lim = tq < nq ? lim_min + row / GQ : 0;   // positions this row sees
+  const int g_full = min(t_end, lim_min) / 16;        // steps every row sees whole
+  const int g_last = (t_end + 15) / 16;
+  int my_phys[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    my_phys[b] = 0;
+    if (g_first + lane * NW < g_last) my_phys[b] = entry[b] < 0 ? 0 : (entry[b] >= a.P ? a.P - 1 : entry[b]);
+  }
+
+  // value tiles during the loop; the cross-wave combine reuses the space
+  __shared__ __attribute__((aligned(16))) char s_v[NW][2][16 * kVRow];
+  static_assert(sizeof(s_v) >= sizeof(float) * NW * R * kD, "combine buffer must fit");
+  float (*s_acc)[R][kD] = reinterpret_cast<float (*)[R][kD]>(&s_v[0][0][0]);
+  __shared__ float s_m[NW][R];
+  __shared__ float s_l[NW][R];
+
+  const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
+  float m = -INFINITY;
+  float ell = 0.0f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // lane loads token `row` of the step, dims 32ks + 8kq .. +7, of K and V
+  auto load_group = [&](int k, uint4 (&K)[4], uint4 (&V)[4], bool tail) {
+    const int g = g_first + k * NW;
+    const int tok = g * 16 + row;
+    int phys = __builtin_amdgcn_readlane(my_phys[0], k);
+    if constexpr (BPG == 2) {
+      const int phys1 = __builtin_amdgcn_readlane(my_phys[1], k);
+      phys = row < 8 ? phys : phys1;
+    }
+    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + kq * 16;
+    const bool ok = !tail || tok < n;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ok) {
+        K[ks] = nt_load16(a.kslab + off + ks * 64);
+        V[ks] = nt_load16(a.vslab + off + ks * 64);
+      } else {
+        K[ks] = make_uint4(0, 0, 0, 0);
+        V[ks] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int buf = 0;
+  auto process_group = [&](int g, const uint4 (&K)[4], const uint4 (&V)[4], bool tail) {
+    const int tok0 = g * 16;
+    char* vb = s_v[wave][buf];
+    buf ^= 1;
+    {
+      const int vrow = (row & 3) * 4 + (row >> 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<uint4*>(vb + vrow * kVRow + (32 * ks + 8 * kq) * 2) = V[ks];
+    }
+    f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st = mfma_k32<BF16>(K[ks], qb[ks], st);
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = st[i] * a.scale_log2;
+      if (tail && tok0 + 4 * kq + i >= lim) sc[i] = -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float f = (m_new == m) ? 1.0f : exp2_fast(m - m_new);
+      m = m_new;
+      ell *= f;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) acc[nb] *= f;
+    }
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pe[i] = (tail && sc[i] == -INFINITY) ? 0.0f : exp2_fast(sc[i] - m);
+      ell += pe[i];
+    }
+    // probabilities as the MFMA's 16-bit operand; bf16 keeps 8 significant
+    // bits, so there the remainder goes in a second product (error ~2^-17)
+    uint2 pb, pl = make_uint2(0, 0);
+    {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = narrow1<BF16>(pe[i]);
+      pb.x = h[0] | (h[1] << 16);
+      pb.y = h[2] | (h[3] << 16);
+      if constexpr (BF16) {
+        uint32_t r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = narrow1<true>(pe[i] - __builtin_bit_cast(float, h[i] << 16));
+        pl.x = r[0] | (r[1] << 16);
+        pl.y = r[2] | (r[3] << 16);
+      }
+    }
+    // the value tile written above by all lanes of the wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(vb);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      // V[token 4kq + i][dim 16nb + row] sits at LDS row i * 4 + kq
+      const int col = 16 * nb + row;
+      uint2 va;
+      va.x = (uint32_t)vt[((0 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((1 * 4 + kq) * kVRow) / 2 + col] << 16);
+      va.y = (uint32_t)vt[((2 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((3 * 4 + kq) * kVRow) / 2 + col] << 16);
+      acc[nb] = mfma_k16<BF16>(va, pb, acc[nb]);
+      if constexpr (BF16) acc[nb] = mfma_k16<BF16>(va, pl, acc[nb]);
+    }
+  };
+
+  {
+    const int ng = g_full > g_first ? (g_full - g_first + NW - 1) / NW : 0;
+    uint4 K0[4], V0[4], K1[4], V1[4];
+    load_group(0, K0, V0, false);
+    if (ng > 0) {
+      int k = 0;
+      for (; k + 2 < ng; k += 2) {
+        load_group(k + 1, K1, V1, false);
+        process_group(g_first + k * NW, K0, V0, false);
+        load_group(k + 2, K0, V0, false);
+        process_group(g_first + (k + 1) * NW, K1, V1, false);
+      }
+      if (k + 2 == ng) {
+        load_group(k + 1, K1, V1, false);
+        process_group(g_first + k * NW, K0, V0, false);
+        process_group(g_first + (k + 1) * NW, K1, V1, false);
+      } else {
+        process_group(g_first + k * NW, K0, V0, false);
+      }
+    }
+    // the steps at the causal edge and the context end, with per-row masks
+    int g = g_full > g_first ? g_first + (g_full - g_first + NW - 1) / NW * NW : g_first;
+    for (; g < g_last; g += NW) {
+      load_group((g - g_first) / NW, K0, V0, true);
+      process_group(g, K0, V0, true);
+    }
+  }
+
+  // ---- combine: the four quarters of a row, then waves ----------------------
+  ell += __shfl_xor(ell, 16);
+  ell += __shfl_xor(ell, 32);
+  __syncthreads();   // every wave is done with its value tiles
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    *reinterpret_cast<float4*>(&s_acc[wave][row][16 * nb + 4 * kq]) =
+        make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+  if (kq == 0) {
+    s_m[wave][row] = m;
+    s_l[wave][row] = ell;
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  const bool worker = t < R * 16;
+  const int wh = t >> 4;
+  const int wc = t & 15;
+  float A[8];
+  float M = -INFINITY, Lsum = 0.0f;
+  if (worker) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][wh]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_m[w][wh];
+      const float wt = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
+      Lsum += wt * s_l[w][wh];
+      const float4 a0 = *reinterpret_cast<const float4*>(&s_acc[w][wh][8 * wc]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s_acc[w][wh][8 * wc + 4]);
+      A[0] += wt * a0.x; A[1] += wt * a0.y; A[2] += wt * a0.z; A[3] += wt * a0.w;
+      A[4] += wt * a1.x; A[5] += wt * a1.y; A[6] += wt * a1.z; A[7] += wt * a1.w;
+    }
+  }
+  const int otq = tile * QT + wh / GQ;
+  const bool live = worker && otq < nq;
+  const size_t orow = (size_t)(q0 + (otq < nq ? otq : 0)) * a.Hq + (size_t)kvh * GQ + wh % GQ;
+  if (nparts == 1) {
+    if (live) {
+      const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = A[i] * inv;
+      *(reinterpret_cast<uint4*>(a.out + orow * kD) + wc) = narrow8<BF16>(o);
+    }
+    return;
+  }
+  if (worker) {
+    const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
+    float4* dst = reinterpret_cast<float4*>(a.ws_acc + ((pbase + p) * R + wh) * kD + 8 * wc);
+    dst[0] = make_float4(A[0], A[1], A[2], A[3]);
+    dst[1] = make_float4(A[4], A[5], A[6], A[7]);
+    if (wc == 0) *reinterpret_cast<float2*>(a.ws_ml + ((pbase + p) * R + wh) * 2) = make_float2(M, Lsum);
+  }
+}
+
 __global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntail) {
   const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -846,8 +1151,41 @@ bool dispatch_g(int G, bool multi, const DecodeArgs& args, dim3 grid, hipStream_
   }
 }
 
-// query tokens per workgroup when a sequence has several queries
-int tile_tokens(int G) { return 8 / G; }
+// Several queries per sequence: rows = query tokens x G query heads per
+// workgroup.  Up to 8 rows per sequence run on the vector path (the decode
+// kernel with a query tile); more run on the matrix cores, 16 rows each.
+struct MqPlan {
+  bool mfma = false;
+  int rows = 8, qt = 1, ntiles = 1;
+};
+
+MqPlan mq_plan(int G, int max_q) {
+  MqPlan p;
+  p.mfma = (int64_t)max_q * G > 8;
+  p.rows = p.mfma ? 16 : 8;
+  p.qt = p.rows / G;
+  p.ntiles = (max_q + p.qt - 1) / p.qt;
+  return p;
+}
+
+template <bool BF16, int GQ, int BS>
+void launch_mq_mfma(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mq_mfma_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
+  if (args.nparts_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, 16, 16 / GQ>), dim3(args.Hkv, args.S, args.ntiles), dim3(16 * 16),
+                       0, stream, args);
+}
+
+template <bool BF16, int BS>
+bool dispatch_mfma(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_mq_mfma<BF16, 1, BS>(args, grid, stream); return true;
+    case 2: launch_mq_mfma<BF16, 2, BS>(args, grid, stream); return true;
+    case 4: launch_mq_mfma<BF16, 4, BS>(args, grid, stream); return true;
+    case 8: launch_mq_mfma<BF16, 8, BS>(args, grid, stream); return true;
+    default: return false;
+  }
+}
 
 }  // namespace
 
@@ -878,15 +1216,16 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
   const bool multi = q_start != nullptr;
-  int ntiles = 1;
+  MqPlan plan;
   if (multi) {
     if (!aligned(q_start, 4)) return fail(PA_ERR_INVALID_ARG, "q_start must be 4-byte aligned");
     if (T < 0 || max_q < 0) return fail(PA_ERR_INVALID_ARG, "negative T or max_q");
     if (T == 0 || max_q == 0) return PA_OK;
-    ntiles = (max_q + tile_tokens(G) - 1) / tile_tokens(G);
-    if (ntiles > 65535) return fail(PA_ERR_UNSUPPORTED, "max_q too large");
+    plan = mq_plan(G, max_q);
+    if (plan.ntiles > 65535) return fail(PA_ERR_UNSUPPORTED, "max_q too large");
   }
-  const int rows = multi ? 8 : G;
+  const int ntiles = plan.ntiles;
+  const int rows = multi ? plan.rows : G;
 
   const LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx);
   const WsLayout wl = ws_layout(S * ntiles, pool->Hkv, rows, cfg);
@@ -931,6 +1270,17 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
+  if (multi && plan.mfma) {
+    switch (pool->B) {
+      case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, args, grid, stream) : dispatch_mfma<false, 8>(G, args, grid, stream); break;
+      case 16: ok = bf16 ? dispatch_mfma<true, 16>(G, args, grid, stream) : dispatch_mfma<false, 16>(G, args, grid, stream); break;
+      case 32: ok = bf16 ? dispatch_mfma<true, 32>(G, args, grid, stream) : dispatch_mfma<false, 32>(G, args, grid, stream); break;
+      case 64: ok = bf16 ? dispatch_mfma<true, 64>(G, args, grid, stream) : dispatch_mfma<false, 64>(G, args, grid, stream); break;
+      default: ok = bf16 ? dispatch_mfma<true, 128>(G, args, grid, stream) : dispatch_mfma<false, 128>(G, args, grid, stream); break;
+    }
+    if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+    return hip_check(hipGetLastError(), "multi-query attention launch");
+  }
   switch (pool->B) {
     case 8: ok = bf16 ? dispatch_g<true, 8>(G, multi, args, grid, stream) : dispatch_g<false, 8>(G, multi, args, grid, stream); break;
     case 16: ok = bf16 ? dispatch_g<true, 16>(G, multi, args, grid, stream) : dispatch_g<false, 16>(G, multi, args, grid, stream); break;
@@ -984,15 +1334,15 @@ size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq, int ma
   if (!pool || S <= 0 || Hq <= 0 || max_ctx < 0 || max_q <= 0 || Hq % pool->Hkv) return 0;
   const int G = Hq / pool->Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
-  const int64_t ntiles = (max_q + tile_tokens(G) - 1) / tile_tokens(G);
-  if (ntiles * S > 0x7fffffff) return 0;
+  const MqPlan plan = mq_plan(G, max_q);
+  if ((int64_t)plan.ntiles * S > 0x7fffffff) return 0;
   // as pa_decode_workspace_bytes: the shortest partition, so the size never
   // decreases with any argument
   LaunchCfg cfg;
   cfg.part_tokens = 16 * kWaves;
   cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
   if (cfg.nparts_max <= 1 && max_ctx > 0) cfg.nparts_max = 2;
-  return ws_layout((int)(S * ntiles), pool->Hkv, 8, cfg).total;
+  return ws_layout(S * plan.ntiles, pool->Hkv, plan.rows, cfg).total;
 }
 
 pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out, const void* q, const int32_t* q_start, int T,

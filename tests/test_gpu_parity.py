@@ -634,3 +634,14 @@ def test_multi_query_workspace_bytes_monotone():
     sizes = [int(lib.pa_multi_query_workspace_bytes(pool.handle, S, 32, ctx, mq))
              for S, ctx, mq in [(4, 1000, 4), (4, 2000, 4), (8, 2000, 4), (8, 2000, 9), (8, 4000, 64)]]
     assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[0] > 0
+
+
+@pytest.mark.parametrize("G,Hkv,B,dtype,max_q", [(1, 4, 16, "f16", 8), (2, 2, 32, "bf16", 4), (4, 2, 16, "bf16", 2),
+                                                 (8, 1, 8, "f16", 1)])
+def test_multi_query_vector_path_few_rows(G, Hkv, B, dtype, max_q):
+    """At most 8 rows (query tokens x heads) per sequence: the vector path."""
+    _say(f"multi-query vector path G={G} max_q={max_q}")
+    rng = np.random.default_rng(500 + G)
+    lens = [3, 40, 129, 700, 2049]
+    nqs = [min(max_q, n) for n in [3, 1, max_q, 2, max_q]]
+    _mq_case(rng, G, Hkv, B, dtype, lens, nqs)
