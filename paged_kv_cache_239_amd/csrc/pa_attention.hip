@@ -1063,6 +1063,212 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
   }
 }
 
+// Many rows per sequence (a chunk of a split prefill): each of the NW waves
+// owns 16 different rows (16 NW per workgroup) and all waves walk the same
+// 16-token steps.  The workgroup loads each key and value tile once into LDS
+// (double-buffered, one barrier per step) and every wave computes its rows
+// from there: K as the A operand read back row-major (272-byte stride:
+// conflict-free 16-byte reads), V transposed as in mq_mfma_kernel.  A wave
+// finishes its rows alone; no cross-wave combine.
+constexpr int kKRow = 272;   // bytes per token row of the LDS key tile (256 + 16 pad)
+
+template <bool BF16, int GQ, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs a) {
+  constexpr int R = 16 * NW;        // rows per workgroup
+  constexpr int QT = R / GQ;        // query tokens per workgroup
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
+  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;
+  static_assert(NW * 64 == 256, "one 16-byte key load and one value load per thread per step");
+
+  int kvh, s, p, tile;
+  {
+    const uint32_t id = blockIdx.x;   // head, then query tile, sequence, partition
+    kvh = id % a.Hkv;
+    uint32_t t = id / a.Hkv;
+    tile = t % a.ntiles;
+    t /= a.ntiles;
+    s = t % a.S;
+    p = t / a.S;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15;
+  const int kq = lane >> 4;
+  const int wrow = wave * 16 + row;  // row of the workgroup
+
+  const int t_begin = p * a.part_tokens;
+  const int step0 = t_begin / 16;
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  int entry[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    const int idx = ((step0 + lane) * 16) / BS + b;   // lane k: the block of step k
+    entry[b] = table[idx < a.maxb ? idx : a.maxb - 1];
+  }
+  const int q0 = min(max(a.q_start[s], 0), a.T);
+  int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
+  const int tq = tile * QT + wrow / GQ;
+  uint4 qb[4];
+  {
+    const bool live = tq < nq;
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        a.q + ((size_t)(live ? q0 + tq : 0) * a.Hq + (size_t)kvh * GQ + wrow % GQ) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
+  }
+
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  nq = __builtin_amdgcn_readfirstlane(nq);
+  if (tile * QT >= nq || nq > n) return;
+  const int lim_min = n - nq + tile * QT + 1;
+  n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
+  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
+  if (p >= nparts) return;
+  const int t_end = min(n, t_begin + a.part_tokens);
+  const int nsteps = (t_end - t_begin + 15) / 16;       // at most 64 (host-side limit)
+  const int lim = tq < nq ? lim_min + wrow / GQ : 0;
+  int my_phys[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    my_phys[b] = 0;
+    if (lane < nsteps) my_phys[b] = entry[b] < 0 ? 0 : (entry[b] >= a.P ? a.P - 1 : entry[b]);
+  }
+
+  __shared__ __attribute__((aligned(16))) char s_k[2][16 * kKRow];
+  __shared__ __attribute__((aligned(16))) char s_v[2][16 * kVRow];
+
+  // this thread's share of a step: token lt = tid / 16, 16 bytes at dims 8 lc
+  const int lt = tid >> 4;
+  const int lc = tid & 15;
+  const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
+  auto load_step = [&](int k, uint4& Kx, uint4& Vx) {
+    const int tok = (step0 + k) * 16 + lt;
+    int phys = __builtin_amdgcn_readlane(my_phys[0], k);
+    if constexpr (BPG == 2) {
+      const int phys1 = __builtin_amdgcn_readlane(my_phys[1], k);
+      phys = lt < 8 ? phys : phys1;
+    }
+    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + lc * 16;
+    if (tok < n) {
+      Kx = nt_load16(a.kslab + off);
+      Vx = nt_load16(a.vslab + off);
+    } else {
+      Kx = make_uint4(0, 0, 0, 0);
+      Vx = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_step = [&](int b, const uint4& Kx, const uint4& Vx) {
+    *reinterpret_cast<uint4*>(s_k[b] + lt * kKRow + lc * 16) = Kx;
+    *reinterpret_cast<uint4*>(s_v[b] + ((lt & 3) * 4 + (lt >> 2)) * kVRow + lc * 16) = Vx;
+  };
+
+  float m = -INFINITY;
+  float ell = 0.0f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint4 Kn, Vn;
+  load_step(0, Kn, Vn);
+  store_step(0, Kn, Vn);
+  if (nsteps > 1) load_step(1, Kn, Vn);
+  __syncthreads();
+  for (int k = 0; k < nsteps; ++k) {
+    const int b = k & 1;
+    const int tok0 = (step0 + k) * 16;
+    // scores: A = K[token row][dims 32ks + 8kq ..] from LDS, B = Q^T
+    f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 kx = *reinterpret_cast<const uint4*>(s_k[b] + row * kKRow + (32 * ks + 8 * kq) * 2);
+      st = mfma_k32<BF16>(kx, qb[ks], st);
+    }
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = st[i] * a.scale_log2;
+      if (tok0 + 4 * kq + i >= lim) sc[i] = -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float f = (m_new == m) ? 1.0f : exp2_fast(m - m_new);
+      m = m_new;
+      ell *= f;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) acc[nb] *= f;
+    }
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pe[i] = (sc[i] == -INFINITY) ? 0.0f : exp2_fast(sc[i] - m);
+      ell += pe[i];
+    }
+    uint2 pb, pl = make_uint2(0, 0);
+    {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = narrow1<BF16>(pe[i]);
+      pb.x = h[0] | (h[1] << 16);
+      pb.y = h[2] | (h[3] << 16);
+      if constexpr (BF16) {
+        uint32_t r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = narrow1<true>(pe[i] - __builtin_bit_cast(float, h[i] << 16));
+        pl.x = r[0] | (r[1] << 16);
+        pl.y = r[2] | (r[3] << 16);
+      }
+    }
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[b]);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const int col = 16 * nb + row;
+      uint2 va;
+      va.x = (uint32_t)vt[((0 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((1 * 4 + kq) * kVRow) / 2 + col] << 16);
+      va.y = (uint32_t)vt[((2 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((3 * 4 + kq) * kVRow) / 2 + col] << 16);
+      acc[nb] = mfma_k16<BF16>(va, pb, acc[nb]);
+      if constexpr (BF16) acc[nb] = mfma_k16<BF16>(va, pl, acc[nb]);
+    }
+    // next step's tiles into the other buffer; the barrier also closes this
+    // step's reads before the buffer is written again
+    if (k + 1 < nsteps) {
+      store_step(b ^ 1, Kn, Vn);
+      if (k + 2 < nsteps) load_step(k + 2, Kn, Vn);
+    }
+    __syncthreads();
+  }
+
+  // ---- this wave's 16 rows: sum the four quarters, then store ---------------
+  ell += __shfl_xor(ell, 16);
+  ell += __shfl_xor(ell, 32);
+  const bool live = tq < nq;
+  if (nparts == 1) {
+    if (live) {
+      const float inv = ell > 0.0f ? 1.0f / ell : 0.0f;
+      uint16_t* orow = a.out + ((size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + wrow % GQ) * kD;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        uint2 w;
+        w.x = narrow1<BF16>(acc[nb][0] * inv) | (narrow1<BF16>(acc[nb][1] * inv) << 16);
+        w.y = narrow1<BF16>(acc[nb][2] * inv) | (narrow1<BF16>(acc[nb][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * kq) = w;
+      }
+    }
+    return;
+  }
+  const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
+  float* dst = a.ws_acc + ((pbase + p) * R + wrow) * kD;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    *reinterpret_cast<float4*>(dst + 16 * nb + 4 * kq) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+  if (kq == 0) *reinterpret_cast<float2*>(a.ws_ml + ((pbase + p) * R + wrow) * 2) = make_float2(m, ell);
+}
+
 __global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntail) {
   const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -1153,19 +1359,33 @@ bool dispatch_g(int G, bool multi, const DecodeArgs& args, dim3 grid, hipStream_
 
 // Several queries per sequence: rows = query tokens x G query heads per
 // workgroup.  Up to 8 rows per sequence run on the vector path (the decode
-// kernel with a query tile); more run on the matrix cores, 16 rows each.
+// kernel with a query tile); up to 32 on the matrix cores with 16 rows per
+// workgroup, its waves splitting the context; more on the matrix cores with
+// 64 rows per workgroup, its waves splitting the rows over shared LDS tiles.
 struct MqPlan {
-  bool mfma = false;
+  bool mfma = false, wide = false;
   int rows = 8, qt = 1, ntiles = 1;
 };
 
 MqPlan mq_plan(int G, int max_q) {
   MqPlan p;
-  p.mfma = (int64_t)max_q * G > 8;
-  p.rows = p.mfma ? 16 : 8;
+  const int64_t need = (int64_t)max_q * G;
+  p.mfma = need > 8;
+  p.wide = need > 32;
+  p.rows = p.wide ? 16 * kWaves : (p.mfma ? 16 : 8);
   p.qt = p.rows / G;
-  p.ntiles = (max_q + p.qt - 1) / p.qt;
+  p.ntiles = (int)((max_q + p.qt - 1) / p.qt);
   return p;
+}
+
+constexpr int kWidePartMax = 16 * 64;   // a lane holds the block of one 16-token step
+
+template <bool BF16, int GQ, int BS>
+void launch_mq_rows(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mq_mfma_rows_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
+  if (args.nparts_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, 16 * kWaves, 16 * kWaves / GQ>), dim3(args.Hkv, args.S, args.ntiles),
+                       dim3(16 * kWaves * 16), 0, stream, args);
 }
 
 template <bool BF16, int GQ, int BS>
@@ -1177,7 +1397,16 @@ void launch_mq_mfma(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
 }
 
 template <bool BF16, int BS>
-bool dispatch_mfma(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+bool dispatch_mfma(int G, bool wide, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
+  if (wide) {
+    switch (G) {
+      case 1: launch_mq_rows<BF16, 1, BS>(args, grid, stream); return true;
+      case 2: launch_mq_rows<BF16, 2, BS>(args, grid, stream); return true;
+      case 4: launch_mq_rows<BF16, 4, BS>(args, grid, stream); return true;
+      case 8: launch_mq_rows<BF16, 8, BS>(args, grid, stream); return true;
+      default: return false;
+    }
+  }
   switch (G) {
     case 1: launch_mq_mfma<BF16, 1, BS>(args, grid, stream); return true;
     case 2: launch_mq_mfma<BF16, 2, BS>(args, grid, stream); return true;
@@ -1227,7 +1456,11 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const int ntiles = plan.ntiles;
   const int rows = multi ? plan.rows : G;
 
-  const LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx);
+  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx);
+  if (multi && plan.wide && cfg.part_tokens > kWidePartMax) {
+    cfg.part_tokens = kWidePartMax;
+    cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
+  }
   const WsLayout wl = ws_layout(S * ntiles, pool->Hkv, rows, cfg);
   char* ws = static_cast<char*>(workspace);
   if (wl.total > 0) {
@@ -1272,11 +1505,11 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const bool bf16 = pool->dtype == PA_BF16;
   if (multi && plan.mfma) {
     switch (pool->B) {
-      case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, args, grid, stream) : dispatch_mfma<false, 8>(G, args, grid, stream); break;
-      case 16: ok = bf16 ? dispatch_mfma<true, 16>(G, args, grid, stream) : dispatch_mfma<false, 16>(G, args, grid, stream); break;
-      case 32: ok = bf16 ? dispatch_mfma<true, 32>(G, args, grid, stream) : dispatch_mfma<false, 32>(G, args, grid, stream); break;
-      case 64: ok = bf16 ? dispatch_mfma<true, 64>(G, args, grid, stream) : dispatch_mfma<false, 64>(G, args, grid, stream); break;
-      default: ok = bf16 ? dispatch_mfma<true, 128>(G, args, grid, stream) : dispatch_mfma<false, 128>(G, args, grid, stream); break;
+      case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 8>(G, plan.wide, args, grid, stream); break;
+      case 16: ok = bf16 ? dispatch_mfma<true, 16>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 16>(G, plan.wide, args, grid, stream); break;
+      case 32: ok = bf16 ? dispatch_mfma<true, 32>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 32>(G, plan.wide, args, grid, stream); break;
+      case 64: ok = bf16 ? dispatch_mfma<true, 64>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 64>(G, plan.wide, args, grid, stream); break;
+      default: ok = bf16 ? dispatch_mfma<true, 128>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 128>(G, plan.wide, args, grid, stream); break;
     }
     if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
     return hip_check(hipGetLastError(), "multi-query attention launch");

@@ -645,3 +645,14 @@ def test_multi_query_vector_path_few_rows(G, Hkv, B, dtype, max_q):
     lens = [3, 40, 129, 700, 2049]
     nqs = [min(max_q, n) for n in [3, 1, max_q, 2, max_q]]
     _mq_case(rng, G, Hkv, B, dtype, lens, nqs)
+
+
+@pytest.mark.parametrize("G,Hkv,B,dtype,max_q", [(1, 2, 16, "bf16", 20), (2, 2, 8, "f16", 12), (4, 2, 32, "bf16", 8),
+                                                 (8, 1, 16, "f16", 4)])
+def test_multi_query_matrix_path_16_rows(G, Hkv, B, dtype, max_q):
+    """9 to 32 rows per sequence: the 16-row matrix-core path (waves split the context)."""
+    _say(f"multi-query 16-row matrix path G={G} max_q={max_q}")
+    rng = np.random.default_rng(700 + G)
+    lens = [max_q, 40, 129, 1000, 2500]
+    nqs = [max_q, 3, max_q, 1, max_q - 1]
+    _mq_case(rng, G, Hkv, B, dtype, lens, nqs)
