@@ -147,6 +147,9 @@ def main() -> int:
     ap.add_argument("--queries", type=int, default=0, metavar="Q",
                     help="instead of one token per sequence: every step appends Q tokens per sequence "
                          "(speculative verification, chunked prefill) and runs multi-query attention")
+    ap.add_argument("--grouped", choices=["auto", "on", "off"], default="auto",
+                    help="read prefixes that several sequences share once per group (auto: for the "
+                         "workloads whose sequences share prompt blocks)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
@@ -189,8 +192,9 @@ def main() -> int:
     W, K = args.warmup, args.steps
     wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
     c = wl.cfg
+    grouped = args.grouped == "on" or (args.grouped == "auto" and c.length_kind == "lognormal_branches")
     eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(W + K),
-                       free_order=wl.free_order)
+                       free_order=wl.free_order, grouped=grouped)
     # seeded N(0,1) pool contents (device RNG), then the prefill history on the native manager
     for layer in range(c.L):
         for which in ("k", "v"):
@@ -351,6 +355,7 @@ def main() -> int:
             "global_batch": wl.S,
             "layers": c.L,
             "block_size": c.B,
+            "shared_prefixes_read_once": bool(grouped),
             "pool_gib": round(eng.pool.nbytes / 2 ** 30, 2),
             "parallelism": "single GPU",
         },
@@ -363,7 +368,8 @@ def main() -> int:
         "attn_launch_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         "attn_launches_timed": int(len(attn_ms)),
         "roofline": {
-            "kernel": f"decode_attention_kernel<{c.dtype},G={c.G},B={c.B}> + merge",
+            "kernel": (f"grouped: mq_mfma_kernel<{c.dtype},group pass> + decode_attention_kernel<suffix> + "
+                       f"cascade merge" if grouped else f"decode_attention_kernel<{c.dtype},G={c.G},B={c.B}> + merge"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -219,6 +219,26 @@ pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables,
                          const int32_t* lens, int32_t S, int32_t maxb,
                          int32_t* pairs, int32_t cap, int32_t* n_pairs);
 
+/* Groups for pa_decode_attention_grouped, from the block tables.  The
+ * batch is cut into runs of consecutive sequences: a run of two or more
+ * sequences whose first block is the same physical block shares the number
+ * of leading table entries all its members agree on, times B, capped at
+ * (shortest member's length - 1) so that every member keeps the position
+ * this step writes for its own pass, and rounded down to a multiple of 16;
+ * every other run shares nothing (length 0), and neighbouring runs that
+ * share nothing are joined.  Host arrays: tables [S][maxb]; lens [S]
+ * (context lengths including this step's token); written: group_start
+ * [S+1] (run g is sequences group_start[g] .. group_start[g+1]-1,
+ * group_start[n_groups] = S), group_len [S] (shared length of each run),
+ * seq_group [S] (the run of each sequence); *n_groups = runs, *max_group =
+ * the largest run that shares, *max_shared = the largest shared length.
+ * No state changes. */
+pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables,
+                           const int32_t* lens, int32_t S, int32_t maxb,
+                           int32_t* group_start, int32_t* group_len,
+                           int32_t* seq_group, int32_t* n_groups,
+                           int32_t* max_group, int32_t* max_shared);
+
 /* ---------------------------------------------------------------------
  * Device operations ("fused block operations" of the reading guide
  * "Efficient Memory Management for Large Language Model Serving with
@@ -342,6 +362,56 @@ pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out,
                                    int max_ctx, int max_q, float scale,
                                    void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
+
+/* Decode attention (optionally with the step's cache write, as
+ * pa_write_kv_decode_attention) for a batch in which groups of consecutive
+ * sequences share a prefix: the parallel samples or beams of one prompt map
+ * the same physical blocks for their first positions ("vLLM PagedAttention
+ * and continuous batching", section "Sharing with reference counts and
+ * copy-on-write"; decode re-reads the cache every step, section "How it
+ * works").  The shared positions are read once per group instead of once
+ * per sequence: a group pass attends every member's query heads to them
+ * (matrix cores), a suffix pass attends each sequence to its own positions,
+ * and the two partial results are merged by the eq. (4) rescale.  Equal to
+ * pa_decode_attention (up to rounding order) when the promise below holds.
+ *   group_start : device int32 [n_groups+1]; group g is sequences
+ *                 group_start[g] .. group_start[g+1]-1 (pa_prefix_groups
+ *                 builds these arrays); groups with a shared length above 0
+ *                 have at most max_group members
+ *   group_len   : device int32 [n_groups]; the group's first group_len[g]
+ *                 positions are mapped to the same physical blocks by every
+ *                 member (the caller's promise) and are below every
+ *                 member's context length.  Used rounded down to a multiple
+ *                 of 16 and at most max_shared; 0 = nothing shared.
+ *   seq_group   : device int32 [S]; the group of each sequence (a value
+ *                 outside [0, n_groups) = none)
+ *   max_suffix  : an upper bound of every sequence's positions outside its
+ *                 group's shared prefix (context length - shared length);
+ *                 positions beyond it are not attended to
+ *   k, v, slot_mapping: as pa_write_kv_decode_attention, or all NULL
+ *   workspace   : >= pa_decode_grouped_workspace_bytes(...) bytes,
+ *                 256-byte aligned (always needed)
+ * Other arguments, shapes and errors as pa_decode_attention.  A broken
+ * promise gives wrong results but no access outside the arguments. */
+pa_status pa_decode_attention_grouped(pa_pool* pool, int layer, const void* k,
+                                      const void* v, const int64_t* slot_mapping,
+                                      void* out, const void* q, int S, int Hq,
+                                      const int32_t* block_tables, int maxb,
+                                      const int32_t* context_lens, int max_ctx,
+                                      const int32_t* group_start,
+                                      const int32_t* group_len,
+                                      const int32_t* seq_group, int n_groups,
+                                      int max_group, int max_shared,
+                                      int max_suffix, float scale,
+                                      void* workspace, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/* Workspace bytes for pa_decode_attention_grouped up to these sizes (never
+ * decreasing in any argument); 0 for invalid sizes. */
+size_t pa_decode_grouped_workspace_bytes(const pa_pool* pool, int S, int Hq,
+                                         int max_ctx, int n_groups,
+                                         int max_group, int max_shared,
+                                         int max_suffix);
 
 /* Workspace bytes for pa_multi_query_attention up to these sizes (never
  * decreasing in any argument); 0 if none is needed or the shape is

@@ -81,6 +81,7 @@ HOST_SIGNATURES = {
     "pa_seq_free": (C.c_int, [P, PI32, I32]),
     "pa_seq_reorder": (C.c_int, [P, PI32, PI32, I32, I32, PI32, I32, PI32, PI32]),
     "pa_move_blocks": (C.c_int, [P, P, PI32, PI32, I32, I32, PI32, I32, PI32]),
+    "pa_prefix_groups": (C.c_int, [P, PI32, PI32, I32, I32, PI32, PI32, PI32, PI32, PI32, PI32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
 }
@@ -98,6 +99,11 @@ DEVICE_SIGNATURES = {
     "pa_multi_query_attention": (C.c_int, [P, C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, P, C.c_int, P,
                                            C.c_int, C.c_int, C.c_float, P, C.c_size_t, P]),
     "pa_multi_query_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int, C.c_int]),
+    "pa_decode_attention_grouped": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P, C.c_int,
+                                              P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, P, C.c_size_t,
+                                              P]),
+    "pa_decode_grouped_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                                       C.c_int]),
 }
 
 _libs = {}

@@ -212,6 +212,13 @@ struct Scores {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// shared positions of group g as every pass of the grouped decode reads them
+__device__ __forceinline__ int shared_positions(const int32_t* grp_len, int ngroups, int max_shared, int g) {
+  if (g < 0 || g >= ngroups) return 0;
+  const int L = min(max(grp_len[g], 0), max_shared);
+  return L & ~15;
+}
+
 // ---------------------------------------------------------------------------
 // decode attention
 // ---------------------------------------------------------------------------
@@ -228,6 +235,16 @@ struct DecodeArgs {
   const int32_t* q_start;   // [S+1] first query row of each sequence (several queries), or null
   int ntiles;               // query tiles per sequence (1 for single-query decode)
   int T;                    // query rows in q and out (several queries; row indices are clamped to it)
+  // shared prefixes read once (grouped decode): sequences of group g are
+  // q_start[g] .. q_start[g+1]-1 in the group pass, their first grp_len[g]
+  // positions (rounded down to 16, at most max_shared) mapped to the same
+  // blocks; seq_group[s] names the group of sequence s (or < 0)
+  const int32_t* grp_len = nullptr;
+  const int32_t* seq_group = nullptr;
+  int ngroups = 0, max_shared = 0;
+  float* gws_ml = nullptr;  // group pass partials [ngroups][gntiles][Hkv][gparts_max][16][2]
+  float* gws_acc = nullptr; // [ngroups][gntiles][Hkv][gparts_max][16][d]
+  int gpart_tokens = 1, gparts_max = 1, gntiles = 0;
   const uint4* knew;        // [S][Hkv][d] this step's keys (fused cache write) or null
   const uint4* vnew;        // [S][Hkv][d] this step's values, or null
   const int64_t* slots;     // [S] their slots, or null
@@ -249,11 +266,15 @@ struct DecodeArgs {
 // at its last positions, each attending causally (up to its own position);
 // a workgroup takes QT of them, and its G rows are (token t, head g) =
 // (row / GQ, row % GQ) with GQ = G / QT query heads per key/value head.
-template <bool BF16, int G, int BS, int NW, int QT>
+// SUF: the suffix pass of the grouped decode -- sequence s attends only to
+// its own positions from the end of its group's shared prefix, and always
+// leaves partials for the cascade merge.
+template <bool BF16, int G, int BS, int NW, int QT, bool SUF = false>
 __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a) {
   using SC = Scores<G>;
   constexpr int GQ = QT > 0 ? G / QT : G;
   static_assert(QT == 0 || GQ * QT == G, "rows = query tokens x query heads");
+  static_assert(NW * 64 >= G * 16, "query staging and the combine use G * 16 threads");
   constexpr int E = SC::E;
   // A 16-token step lies inside one block when 16 | BS; with 8-token blocks
   // it covers two (loads 0-1 read the first, loads 2-3 the second).
@@ -296,7 +317,14 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   // Requests that do not depend on the context length go out first: the
   // query group and this lane's block-table entry (index clamped into the
   // table row; an entry past the sequence is never used).
-  const int t_begin = p * a.part_tokens;
+  int start = 0;   // first position of this pass (the suffix pass starts after the shared prefix)
+  if constexpr (SUF) {
+    int n0 = a.lens[s];
+    n0 = n0 < 0 ? 0 : (n0 > a.max_ctx ? a.max_ctx : n0);
+    start = __builtin_amdgcn_readfirstlane(
+        min(shared_positions(a.grp_len, a.ngroups, a.max_shared, a.seq_group[s]), n0));
+  }
+  const int t_begin = start + p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
   const int32_t* table = a.tables + (size_t)s * a.maxb;
   uint4 qv = make_uint4(0, 0, 0, 0);
@@ -334,7 +362,8 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     n = n - nq + min(tile * QT + QT, nq);
   }
   n = __builtin_amdgcn_readfirstlane(n);
-  const int nparts = n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1;
+  const int nparts = SUF ? (n - start + a.part_tokens - 1) / a.part_tokens
+                         : (n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1);
   if (p >= nparts) return;
   const int t_end = min(n, t_begin + a.part_tokens);
 
@@ -661,7 +690,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     live = worker && tq < nq;
   }
   uint4* out_row = reinterpret_cast<uint4*>(a.out + orow * kD) + wc;
-  if (nparts == 1) {
+  if (!SUF && nparts == 1) {
     if (live) {
       const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
       float o[8];
@@ -759,6 +788,66 @@ __global__ __launch_bounds__(G * 16) void decode_merge_kernel(const DecodeArgs a
 }
 
 // ---------------------------------------------------------------------------
+// cascade merge of the grouped decode: for sequence s and each query head of
+// key/value head kvh, the partials of its group's shared prefix (rows
+// member * G + head of the group pass) and of its own suffix, combined by the
+// eq. (4) rescale; thread = (head, 8-dim chunk)
+// ---------------------------------------------------------------------------
+template <bool BF16, int G>
+__global__ __launch_bounds__(G * 16) void cascade_merge_kernel(const DecodeArgs a) {
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int wh = threadIdx.x >> 4;
+  const int wc = threadIdx.x & 15;
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int g = a.seq_group[s];
+  const int L = min(shared_positions(a.grp_len, a.ngroups, a.max_shared, g), n);
+  float Mg = -INFINITY, Lg = 0.0f, Ag[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Ag[i] = 0.0f;
+  auto add = [&](const float* ml, const float* acc) {
+    const float2 x = *reinterpret_cast<const float2*>(ml);
+    if (x.x == -INFINITY) return;
+    const float4 a0 = *reinterpret_cast<const float4*>(acc);
+    const float4 a1 = *reinterpret_cast<const float4*>(acc + 4);
+    const float M = fmaxf(Mg, x.x);
+    const float fo = (Mg == -INFINITY) ? 0.0f : exp2_fast(Mg - M);
+    const float fn = exp2_fast(x.x - M);
+    Lg = fo * Lg + fn * x.y;
+    Ag[0] = fo * Ag[0] + fn * a0.x; Ag[1] = fo * Ag[1] + fn * a0.y;
+    Ag[2] = fo * Ag[2] + fn * a0.z; Ag[3] = fo * Ag[3] + fn * a0.w;
+    Ag[4] = fo * Ag[4] + fn * a1.x; Ag[5] = fo * Ag[5] + fn * a1.y;
+    Ag[6] = fo * Ag[6] + fn * a1.z; Ag[7] = fo * Ag[7] + fn * a1.w;
+    Mg = M;
+  };
+  if (L > 0) {
+    // the group pass wrote this sequence's rows as query token (member) w
+    const int first = min(max(a.q_start[g], 0), a.S);
+    const int w = s - first;
+    const int r = w * G + wh;                     // row among the group's rows
+    const int tile = r / 16, row = r % 16;
+    if (w >= 0 && tile < a.gntiles) {
+      const int np = (L + a.gpart_tokens - 1) / a.gpart_tokens;
+      const size_t base = (((size_t)g * a.gntiles + tile) * a.Hkv + kvh) * (size_t)a.gparts_max;
+      for (int pp = 0; pp < np; ++pp)
+        add(a.gws_ml + ((base + pp) * 16 + row) * 2, a.gws_acc + ((base + pp) * 16 + row) * kD + 8 * wc);
+    }
+  }
+  if (n > L) {
+    const int np = (n - L + a.part_tokens - 1) / a.part_tokens;
+    const size_t base = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
+    for (int pp = 0; pp < np; ++pp)
+      add(a.ws_ml + ((base + pp) * G + wh) * 2, a.ws_acc + ((base + pp) * G + wh) * kD + 8 * wc);
+  }
+  const float inv = Lg > 0.0f ? 1.0f / Lg : 0.0f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = Ag[i] * inv;
+  *(reinterpret_cast<uint4*>(a.out + ((size_t)s * a.Hq + (size_t)kvh * G + wh) * kD) + wc) = narrow8<BF16>(o);
+}
+
+// ---------------------------------------------------------------------------
 // several queries per sequence on the matrix cores
 //
 // A workgroup's 16 rows are QT = 16 / GQ query tokens x GQ query heads of one
@@ -806,7 +895,11 @@ __device__ __forceinline__ f32x4_t mfma_k16(const uint2 a, const uint2 b, f32x4_
 
 constexpr int kVRow = 288;   // bytes per token row of the LDS value tile (256 + 32 pad)
 
-template <bool BF16, int GQ, int BS, int NW>
+// GRP: the group pass of the grouped decode -- "sequence" s is group s, its
+// query tokens are the group's sequences (one query each), every row sees the
+// group's shared positions, read through the first member's table, and the
+// result is always left as partials for the cascade merge.
+template <bool BF16, int GQ, int BS, int NW, bool GRP = false>
 __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
   constexpr int R = 16;             // rows per workgroup
   constexpr int QT = R / GQ;        // query tokens per workgroup
@@ -830,15 +923,16 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
 
   const int t_begin = p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
-  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  const int q0 = min(max(a.q_start[s], 0), a.T);
+  int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
+  // a group reads its shared positions through its first member's table
+  const int32_t* table = a.tables + (size_t)(GRP ? min(q0, a.T - 1) : s) * a.maxb;
   int entry[BPG];
 #pragma unroll
   for (int b = 0; b < BPG; ++b) {
     const int idx = ((g_first + lane * NW) * 16) / BS + b;
     entry[b] = table[idx < a.maxb ? idx : a.maxb - 1];
   }
-  const int q0 = min(max(a.q_start[s], 0), a.T);
-  int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
   const int tq = tile * QT + row / GQ;    // this lane's query token
   uint4 qb[4];
   {
@@ -849,16 +943,23 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) qb[ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
   }
 
-  int n = a.lens[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  int n, lim_min;
   nq = __builtin_amdgcn_readfirstlane(nq);
-  if (tile * QT >= nq || nq > n) return;
-  const int lim_min = n - nq + tile * QT + 1;
-  n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
+  if constexpr (GRP) {
+    n = __builtin_amdgcn_readfirstlane(shared_positions(a.grp_len, a.ngroups, a.max_shared, s));
+    if (tile * QT >= nq || n == 0) return;
+    lim_min = n;                                        // no causal edge: every row sees all n
+  } else {
+    n = a.lens[s];
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    if (tile * QT >= nq || nq > n) return;
+    lim_min = n - nq + tile * QT + 1;
+    n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
+  }
   const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
   if (p >= nparts) return;
   const int t_end = min(n, t_begin + a.part_tokens);
-  const int lim = tq < nq ? lim_min + row / GQ : 0;   // positions this row sees
+  const int lim = tq < nq ? (GRP ? n : lim_min + row / GQ) : 0;   // positions this row sees
   const int g_full = min(t_end, lim_min) / 16;        // steps every row sees whole
   const int g_last = (t_end + 15) / 16;
   int my_phys[BPG];
@@ -1044,7 +1145,7 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
   const int otq = tile * QT + wh / GQ;
   const bool live = worker && otq < nq;
   const size_t orow = (size_t)(q0 + (otq < nq ? otq : 0)) * a.Hq + (size_t)kvh * GQ + wh % GQ;
-  if (nparts == 1) {
+  if (!GRP && nparts == 1) {
     if (live) {
       const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
       float o[8];
@@ -1525,6 +1626,181 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   return hip_check(hipGetLastError(), "decode attention launch");
 }
 
+// Grouped decode: the group pass (shared prefixes, 16-row matrix-core
+// kernel over each group's members), the suffix pass (the decode kernel from
+// each sequence's first own position, with the fused cache write when slots
+// are given), then the cascade merge.
+struct GroupedLayout {
+  LaunchCfg gcfg, scfg;
+  int gntiles = 0;
+  size_t g_ml = 0, g_acc = 0, s_ml = 0, s_acc = 0, total = 0;
+};
+
+// The suffix pass runs one-wave workgroups (two for G = 8: the kernel stages
+// the query and combines with G * 16 threads): suffixes are short (the tail
+// of a prompt's last block plus the tokens generated since the fork).
+constexpr int suffix_waves(int G) { return G <= 4 ? 1 : 2; }
+constexpr int kSuffixPart = 16 * 16;   // 16 steps of 16 tokens per partition
+
+GroupedLayout grouped_layout(int S, int Hkv, int G, int max_suffix, int ngroups, int max_group, int max_shared,
+                             bool shortest) {
+  GroupedLayout w;
+  w.gntiles = ngroups > 0 ? (int)(((int64_t)max_group * G + 15) / 16) : 0;
+  if (shortest) {   // the shortest partition the launcher can pick: a bound for every call
+    w.gcfg.part_tokens = 16 * kWaves;
+  } else {
+    w.gcfg = choose_launch(ngroups * w.gntiles, Hkv, max_shared);
+  }
+  w.scfg.part_tokens = kSuffixPart;
+  w.gcfg.nparts_max = max_shared > 0 ? (max_shared + w.gcfg.part_tokens - 1) / w.gcfg.part_tokens : 1;
+  w.scfg.nparts_max = max_suffix > 0 ? (max_suffix + w.scfg.part_tokens - 1) / w.scfg.part_tokens : 1;
+  const size_t gunits = (size_t)ngroups * w.gntiles * Hkv * w.gcfg.nparts_max * 16;
+  const size_t sunits = (size_t)S * Hkv * w.scfg.nparts_max * G;
+  w.g_ml = 0;
+  w.g_acc = w.g_ml + align_up(gunits * 2 * sizeof(float), 256);
+  w.s_ml = w.g_acc + align_up(gunits * kD * sizeof(float), 256);
+  w.s_acc = w.s_ml + align_up(sunits * 2 * sizeof(float), 256);
+  w.total = w.s_acc + align_up(sunits * kD * sizeof(float), 256);
+  return w;
+}
+
+template <bool BF16, int G, int BS>
+void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3 sgrid, const DecodeArgs& ma,
+                    hipStream_t stream) {
+  if (ggrid.x > 0)
+    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kWaves, true>), ggrid, dim3(kWaves * 64), 0, stream, ga);
+  constexpr int NWS = suffix_waves(G);
+  static_assert(NWS * 64 >= G * 16, "the decode kernel needs G * 16 threads");
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa);
+  hipLaunchKernelGGL((cascade_merge_kernel<BF16, G>), dim3(ma.Hkv, ma.S), dim3(G * 16), 0, stream, ma);
+}
+
+template <bool BF16, int BS>
+bool dispatch_grouped(int G, const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3 sgrid, const DecodeArgs& ma,
+                      hipStream_t stream) {
+  switch (G) {
+    case 1: launch_grouped<BF16, 1, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
+    case 2: launch_grouped<BF16, 2, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
+    case 4: launch_grouped<BF16, 4, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
+    case 8: launch_grouped<BF16, 8, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
+    default: return false;
+  }
+}
+
+pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int S, int Hq,
+                         const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx,
+                         const int32_t* group_start, const int32_t* group_len, const int32_t* seq_group, int ngroups,
+                         int max_group, int max_shared, int max_suffix, float scale, void* workspace, size_t ws_bytes,
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping, hipStream_t stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
+  if (S == 0) return PA_OK;
+  if (Hq <= 0 || Hq % pool->Hkv) return fail(PA_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+  const int G = Hq / pool->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PA_ERR_UNSUPPORTED, "Hq / Hkv must be 1, 2, 4 or 8");
+  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
+  if (pool->B != 8 && pool->B != 16 && pool->B != 32 && pool->B != 64 && pool->B != 128)
+    return fail(PA_ERR_UNSUPPORTED, "block size must be 8, 16, 32, 64 or 128");
+  if (!out || !q || !block_tables || !context_lens || !seq_group) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(seq_group, 4))
+    return fail(PA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  if (maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad maxb or max_ctx");
+  if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (S > 65535 || pool->Hkv > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences and heads");
+  if (ngroups < 0 || max_group < 0 || max_shared < 0) return fail(PA_ERR_INVALID_ARG, "negative group sizes");
+  if (ngroups > 0 && (!group_start || !group_len || !aligned(group_start, 4) || !aligned(group_len, 4)))
+    return fail(PA_ERR_INVALID_ARG, "group_start and group_len must be 4-byte aligned device pointers");
+  if (ngroups > 65535 || max_group > S) return fail(PA_ERR_INVALID_ARG, "bad ngroups or max_group");
+  if (max_shared > max_ctx) return fail(PA_ERR_INVALID_ARG, "max_shared exceeds max_ctx");
+  if (max_suffix < 0 || max_suffix > max_ctx) return fail(PA_ERR_INVALID_ARG, "bad max_suffix");
+  if (k_new || v_new || slot_mapping) {
+    if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "k, v and slot_mapping go together");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
+  }
+  const GroupedLayout wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false);
+  char* ws = static_cast<char*>(workspace);
+  if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_grouped_workspace_bytes");
+
+  DecodeArgs args;
+  args.kslab = pool->k_slab(layer);
+  args.vslab = pool->v_slab(layer);
+  args.tile_bytes = pool->tile_bytes;
+  args.q = static_cast<const uint16_t*>(q);
+  args.out = static_cast<uint16_t*>(out);
+  args.tables = block_tables;
+  args.lens = context_lens;
+  args.S = S;
+  args.Hq = Hq;
+  args.Hkv = pool->Hkv;
+  args.P = pool->P;
+  args.maxb = maxb;
+  args.max_ctx = max_ctx;
+  args.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  args.knew = nullptr;
+  args.vnew = nullptr;
+  args.slots = nullptr;
+  args.nslots = (int64_t)pool->P * pool->B;
+  args.q_start = group_start;   // the merge finds each group's first member here
+  args.ntiles = 1;
+  args.T = S;
+  args.grid_order = 0;
+  args.pstride = 1;
+  args.grp_len = group_len;
+  args.seq_group = seq_group;
+  args.ngroups = ngroups;
+  args.max_shared = max_shared;
+  args.gws_ml = reinterpret_cast<float*>(ws + wl.g_ml);
+  args.gws_acc = reinterpret_cast<float*>(ws + wl.g_acc);
+  args.gpart_tokens = wl.gcfg.part_tokens;
+  args.gparts_max = wl.gcfg.nparts_max;
+  args.gntiles = wl.gntiles;
+  args.ws_ml = reinterpret_cast<float*>(ws + wl.s_ml);
+  args.ws_acc = reinterpret_cast<float*>(ws + wl.s_acc);
+  args.part_tokens = wl.scfg.part_tokens;
+  args.nparts_max = wl.scfg.nparts_max;
+
+  // group pass: "sequences" are the groups, query tokens their members
+  DecodeArgs ga = args;
+  ga.S = ngroups;
+  ga.q_start = group_start;
+  ga.ntiles = wl.gntiles;
+  ga.part_tokens = wl.gcfg.part_tokens;
+  ga.nparts_max = wl.gcfg.nparts_max;
+  ga.ws_ml = args.gws_ml;
+  ga.ws_acc = args.gws_acc;
+  const uint64_t gwg = (ngroups > 0 && max_shared >= 16)
+                           ? (uint64_t)pool->Hkv * ngroups * wl.gntiles * wl.gcfg.nparts_max : 0;
+  // suffix pass (with this step's cache write, if given)
+  DecodeArgs sa = args;
+  sa.knew = static_cast<const uint4*>(k_new);
+  sa.vnew = static_cast<const uint4*>(v_new);
+  sa.slots = slot_mapping;
+  const uint64_t swg = (uint64_t)pool->Hkv * S * wl.scfg.nparts_max;
+  if (gwg > 0x7fffffffULL || swg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const dim3 ggrid((unsigned)gwg), sgrid((unsigned)swg);
+  bool ok;
+  const bool bf16 = pool->dtype == PA_BF16;
+  switch (pool->B) {
+    case 8: ok = bf16 ? dispatch_grouped<true, 8>(G, ga, ggrid, sa, sgrid, args, stream)
+                      : dispatch_grouped<false, 8>(G, ga, ggrid, sa, sgrid, args, stream); break;
+    case 16: ok = bf16 ? dispatch_grouped<true, 16>(G, ga, ggrid, sa, sgrid, args, stream)
+                       : dispatch_grouped<false, 16>(G, ga, ggrid, sa, sgrid, args, stream); break;
+    case 32: ok = bf16 ? dispatch_grouped<true, 32>(G, ga, ggrid, sa, sgrid, args, stream)
+                       : dispatch_grouped<false, 32>(G, ga, ggrid, sa, sgrid, args, stream); break;
+    case 64: ok = bf16 ? dispatch_grouped<true, 64>(G, ga, ggrid, sa, sgrid, args, stream)
+                       : dispatch_grouped<false, 64>(G, ga, ggrid, sa, sgrid, args, stream); break;
+    default: ok = bf16 ? dispatch_grouped<true, 128>(G, ga, ggrid, sa, sgrid, args, stream)
+                       : dispatch_grouped<false, 128>(G, ga, ggrid, sa, sgrid, args, stream); break;
+  }
+  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+  return hip_check(hipGetLastError(), "grouped decode attention launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1601,6 +1877,26 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, 
   }
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
                        ws_bytes, k, v, slot_mapping, nullptr, 0, 0, stream);
+}
+
+size_t pa_decode_grouped_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx, int n_groups,
+                                        int max_group, int max_shared, int max_suffix) {
+  if (!pool || S <= 0 || Hq <= 0 || max_ctx < 0 || Hq % pool->Hkv || n_groups < 0 || max_group < 0 ||
+      max_shared < 0 || max_group > S || max_shared > max_ctx || max_suffix < 0 || max_suffix > max_ctx)
+    return 0;
+  return grouped_layout(S, pool->Hkv, Hq / pool->Hkv, max_suffix, n_groups, max_group, max_shared, true).total;
+}
+
+pa_status pa_decode_attention_grouped(pa_pool* pool, int layer, const void* k, const void* v,
+                                      const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+                                      const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx,
+                                      const int32_t* group_start, const int32_t* group_len, const int32_t* seq_group,
+                                      int n_groups, int max_group, int max_shared, int max_suffix, float scale,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  return grouped_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, group_start, group_len,
+                        seq_group, n_groups, max_group, max_shared, max_suffix, scale, workspace, ws_bytes, k, v,
+                        slot_mapping, stream);
 }
 
 }  // extern "C"

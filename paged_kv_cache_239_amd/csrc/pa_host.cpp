@@ -509,4 +509,61 @@ pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables, const int3
   return PA_OK;
 }
 
+pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t S, int32_t maxb,
+                           int32_t* group_start, int32_t* group_len, int32_t* seq_group, int32_t* n_groups,
+                           int32_t* max_group, int32_t* max_shared) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (S < 0 || maxb < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (!n_groups || !max_group || !max_shared || !group_start) return fail(PA_ERR_INVALID_ARG, "NULL output");
+  if (S > 0 && (!tables || !lens || !group_len || !seq_group)) return fail(PA_ERR_INVALID_ARG, "NULL array");
+  const int B = pool->B;
+  for (int32_t s = 0; s < S; ++s)
+    if (lens[s] < 0 || ((int64_t)lens[s] + B - 1) / B > maxb) return fail(PA_ERR_INVALID_ARG, "length outside the table");
+  // runs of consecutive sequences with the same first block; a run of one,
+  // or one whose shared length rounds to 0, shares nothing.  Consecutive
+  // runs that share nothing are joined into one.
+  int32_t ng = 0, mg = 0, ms = 0;
+  int32_t i = 0;
+  while (i < S) {
+    int32_t j = i + 1;
+    if (lens[i] > 0)
+      while (j < S && lens[j] > 0 && tables[(size_t)j * maxb] == tables[(size_t)i * maxb]) ++j;
+    int32_t L = 0;
+    if (j - i >= 2) {
+      int32_t nb = maxb, nmin = lens[i];
+      for (int32_t m = i; m < j; ++m) {
+        nb = std::min<int32_t>(nb, (lens[m] + B - 1) / B);
+        nmin = std::min(nmin, lens[m]);
+      }
+      int32_t k = 0;
+      while (k < nb) {
+        bool same = true;
+        for (int32_t m = i + 1; m < j && same; ++m) same = tables[(size_t)m * maxb + k] == tables[(size_t)i * maxb + k];
+        if (!same) break;
+        ++k;
+      }
+      L = (int32_t)std::min<int64_t>((int64_t)k * B, (int64_t)nmin - 1) & ~15;
+    }
+    if (L == 0 && ng > 0 && group_len[ng - 1] == 0) {
+      // extend the previous run that shares nothing
+    } else {
+      group_start[ng] = i;
+      group_len[ng] = L;
+      ++ng;
+    }
+    for (int32_t m = i; m < j; ++m) seq_group[m] = ng - 1;
+    if (L > 0) {
+      mg = std::max(mg, j - i);
+      ms = std::max(ms, L);
+    }
+    i = j;
+  }
+  group_start[ng] = S;
+  *n_groups = ng;
+  *max_group = mg;
+  *max_shared = ms;
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -11,7 +11,10 @@ Per step (batch of S sequences, each appending one token):
   3. pa_copy_blocks for the copy-on-write pairs, before any write;
   4. for every layer: the new token's cache write and the attention, in one
      pass (pa_write_kv_decode_attention) or as pa_write_kv then
-     pa_decode_attention.
+     pa_decode_attention.  With ``grouped``, sequences that share leading
+     blocks (parallel samples, beams) are found after the appends
+     (pa_prefix_groups) and their shared positions are read once per group
+     (pa_decode_attention_grouped).
 
 Everything in steps 1, 3 and 4 runs in the native library; this module only
 sequences the calls and moves arguments.
@@ -54,10 +57,12 @@ class _Staging:
 
 class DecodeEngine:
     def __init__(self, L: int, Hq: int, Hkv: int, d: int, B: int, P: int, dtype: str, S: int, maxb: int,
-                 free_order: Optional[Sequence[int]] = None, device: str = "cuda", fused: bool = True):
+                 free_order: Optional[Sequence[int]] = None, device: str = "cuda", fused: bool = True,
+                 grouped: bool = False):
         import torch
         self.torch = torch
         self.fused = fused
+        self.grouped = grouped
         self.L, self.Hq, self.Hkv, self.d, self.B, self.P = L, Hq, Hkv, d, B, P
         self.S, self.maxb = S, maxb
         self.device = device
@@ -68,7 +73,15 @@ class DecodeEngine:
         self.d_lens = torch.zeros(S, dtype=torch.int32, device=device)
         self.d_slots = torch.zeros(S, dtype=torch.int64, device=device)
         self.d_pairs = torch.zeros((S, 2), dtype=torch.int32, device=device)
-        self._stage_bytes = S * maxb * 4 + S * 4 + S * 8 + S * 8
+        # shared-prefix runs of the current step (grouped mode)
+        self.d_group_start = torch.zeros(S + 1, dtype=torch.int32, device=device)
+        self.d_group_len = torch.zeros(S, dtype=torch.int32, device=device)
+        self.d_seq_group = torch.zeros(S, dtype=torch.int32, device=device)
+        self.n_groups = self.max_group = self.max_shared = self.max_suffix = 0
+        self.gws = None
+        self.gws_bytes = 0
+        self._gcap = 0
+        self._stage_bytes = S * maxb * 4 + S * 4 + S * 8 + S * 8 + (3 * S + 1) * 4
         self._staging = _Staging(self._stage_bytes)
         self.ws = None
         self.ws_bytes = 0
@@ -120,12 +133,17 @@ class DecodeEngine:
         self.lens += 1
         self.last_slots, self.last_pairs = slots, pairs
         S, mb = self.S, self.maxb
+        if self.grouped:
+            gs, gl, sg, self.max_group, self.max_shared = self.pool.prefix_groups(self.tables, self.lens)
+            self.n_groups = len(gl)
+            self.max_suffix = int(np.max(self.lens - gl[sg])) if S else 0
         j, buf = self._staging.next()
         o = 0
         tb = buf[o:o + S * mb * 4]; o += S * mb * 4
         lb = buf[o:o + S * 4]; o += S * 4
         sb = buf[o:o + S * 8]; o += S * 8
-        pb = buf[o:o + S * 8]
+        pb = buf[o:o + S * 8]; o += S * 8
+        gb = buf[o:o + (3 * S + 1) * 4]
         tb.numpy().view(np.int32)[:] = self.tables.reshape(-1)
         lb.numpy().view(np.int32)[:] = self.lens
         sb.numpy().view(np.int64)[:] = slots
@@ -133,14 +151,39 @@ class DecodeEngine:
         if npairs:
             pb.numpy().view(np.int32)[: 2 * npairs] = pairs.reshape(-1)
         st = torch.cuda.current_stream() if stream is None else stream
+        if self.grouped:
+            g = gb.numpy().view(np.int32)
+            ng = self.n_groups
+            g[: ng + 1] = gs
+            g[S + 1: S + 1 + ng] = gl
+            g[2 * S + 1: 3 * S + 1] = sg
         with torch.cuda.stream(st):
             self.d_tables.view(-1).view(torch.uint8).copy_(tb, non_blocking=True)
             self.d_lens.view(torch.uint8).copy_(lb, non_blocking=True)
             self.d_slots.view(torch.uint8).copy_(sb, non_blocking=True)
             if npairs:
                 self.d_pairs[:npairs].view(-1).view(torch.uint8).copy_(pb[: 8 * npairs], non_blocking=True)
+            if self.grouped:
+                gi = gb.view(torch.int32)
+                self.d_group_start.copy_(gi[: S + 1], non_blocking=True)
+                self.d_group_len.copy_(gi[S + 1: 2 * S + 1], non_blocking=True)
+                self.d_seq_group.copy_(gi[2 * S + 1: 3 * S + 1], non_blocking=True)
         self._staging.mark(j, st)
         return int(self.lens.max())
+
+    def ensure_grouped_workspace(self, stream=None) -> None:
+        # sized for any run count, shared length up to the table width, and
+        # runs up to the next power of two above the largest one so far
+        cap = max(2, 1 << (max(self.max_group, 1) - 1).bit_length())
+        if cap <= self._gcap and self.gws is not None:
+            return
+        full = self.maxb * self.B
+        need = self.pool.grouped_workspace_bytes(self.S, self.Hq, full, self.S, min(cap, self.S), full, full)
+        torch = self.torch
+        self.gws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        check(self.pool.lib, self.pool.lib.pa_decode_workspace_init(_ptr(self.gws), need, _stream_handle(stream)))
+        self.gws_bytes = need
+        self._gcap = cap
 
     def device_step(self, qs: List, knews: List, vnews: List, outs: List, max_ctx: int, scale: float,
                     stream=None, layers: Optional[Sequence[int]] = None, attn_events=None,
@@ -155,6 +198,9 @@ class DecodeEngine:
         if npairs and not skip_copies:
             self.pool.copy_blocks(self.d_pairs[:npairs], stream=stream)
         self.ensure_workspace(max_ctx, stream)
+        grouped = self.grouped and self.max_shared > 0
+        if grouped:
+            self.ensure_grouped_workspace(stream)
         torch = self.torch
         st = None
         if attn_events is not None:
@@ -169,7 +215,15 @@ class DecodeEngine:
                 else:
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(st)
-            if self.fused:
+            if grouped:
+                fused = self.fused
+                self.pool.decode_attention_grouped(
+                    layer, outs[layer], qs[layer], self.d_tables, self.d_lens, max_ctx,
+                    self.d_group_start[: self.n_groups + 1], self.d_group_len[: self.n_groups], self.d_seq_group,
+                    self.max_group, self.max_shared, self.max_suffix, scale, self.gws,
+                    k=knews[layer] if fused else None, v=vnews[layer] if fused else None,
+                    slot_mapping=self.d_slots if fused else None, stream=stream)
+            elif self.fused:
                 self.pool.write_kv_decode_attention(layer, knews[layer], vnews[layer], self.d_slots, outs[layer],
                                                     qs[layer], self.d_tables, self.d_lens, max_ctx, scale,
                                                     workspace=self.ws, stream=stream)

@@ -213,6 +213,22 @@ class Pool:
                                                 _i32p(out), _i32p(out_lens)))
         return out[:S_new], out_lens[:S_new]
 
+    def prefix_groups(self, tables: np.ndarray, lens):
+        """Runs of sequences sharing leading blocks (pa_prefix_groups).
+        Returns (group_start int32 [n+1], group_len int32 [n], seq_group int32
+        [S], max_group, max_shared)."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
+        S, maxb = tables.shape
+        ln = _as_i32(lens)
+        gs = np.zeros(S + 1, dtype=np.int32)
+        gl = np.zeros(max(S, 1), dtype=np.int32)
+        sg = np.zeros(max(S, 1), dtype=np.int32)
+        ng, mg, ms = C.c_int32(), C.c_int32(), C.c_int32()
+        check(self.lib, self.lib.pa_prefix_groups(self.handle, _i32p(tables), _i32p(ln), S, maxb, _i32p(gs), _i32p(gl),
+                                                  _i32p(sg), C.byref(ng), C.byref(mg), C.byref(ms)))
+        n = ng.value
+        return gs[: n + 1].copy(), gl[:n].copy(), sg[:S].copy(), mg.value, ms.value
+
     def move_blocks(self, to: "Pool", tables: np.ndarray, lens) -> np.ndarray:
         """Swap a group of sequences from this pool to ``to`` (host manager):
         ``tables`` (int32 [S][maxb]) are rewritten in place to name blocks of
@@ -277,6 +293,31 @@ class Pool:
             self.handle, layer, _ptr(out), _ptr(q), _ptr(q_start), T, S, Hq, _ptr(block_tables), maxb,
             _ptr(context_lens), int(max_ctx), int(max_q), C.c_float(scale), C.c_void_p(ws_ptr or None),
             C.c_size_t(ws_bytes), _stream_handle(stream)))
+
+    def grouped_workspace_bytes(self, S: int, Hq: int, max_ctx: int, n_groups: int, max_group: int,
+                                max_shared: int, max_suffix: int) -> int:
+        return int(self.lib.pa_decode_grouped_workspace_bytes(self.handle, S, Hq, max_ctx, n_groups, max_group,
+                                                              max_shared, max_suffix))
+
+    def decode_attention_grouped(self, layer: int, out, q, block_tables, context_lens, max_ctx: int, group_start,
+                                 group_len, seq_group, max_group: int, max_shared: int, max_suffix: int,
+                                 scale: float, workspace, k=None, v=None, slot_mapping=None, stream=None) -> None:
+        """Decode attention reading each group's shared prefix once (see
+        pa_decode_attention_grouped); with k, v, slot_mapping the step's
+        cache write is done in the same pass.  group_start: device int32
+        [n_groups+1]; group_len: device int32 [n_groups]; seq_group: device
+        int32 [S]."""
+        S, Hq = int(q.shape[0]), int(q.shape[1])
+        maxb = int(block_tables.shape[1])
+        ng = int(group_start.shape[0]) - 1
+        kp = _ptr(k) if k is not None else None
+        vp = _ptr(v) if v is not None else None
+        sp = _ptr(slot_mapping) if slot_mapping is not None else None
+        check(self.lib, self.lib.pa_decode_attention_grouped(
+            self.handle, layer, C.c_void_p(kp), C.c_void_p(vp), C.c_void_p(sp), _ptr(out), _ptr(q), S, Hq,
+            _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), _ptr(group_start), _ptr(group_len),
+            _ptr(seq_group), ng, int(max_group), int(max_shared), int(max_suffix), C.c_float(scale), _ptr(workspace),
+            C.c_size_t(int(workspace.numel())), _stream_handle(stream)))
 
     def write_kv_decode_attention(self, layer: int, k, v, slot_mapping, out, q, block_tables, context_lens,
                                   max_ctx: int, scale: float, workspace=None, stream=None) -> None:

@@ -96,10 +96,10 @@ def test_copy_blocks_bit_exact(dtype, B, Hkv, L):
 # --------------------------------------------------------------------------------
 # decode attention on the small workloads: full step vs oracle
 # --------------------------------------------------------------------------------
-def _small_workload_step(cfg, steps=1, fused=True, block_size=None):
+def _small_workload_step(cfg, steps=1, fused=True, block_size=None, grouped=False):
     wl = with_headroom(make_workload(cfg, block_size=block_size), steps)
     c = wl.cfg
-    eng = make_engine(wl, steps=steps, fused=fused)
+    eng = make_engine(wl, steps=steps, fused=fused, grouped=grouped)
     fill_pool_nan(eng, c.dtype)                 # unwritten slots hold NaN
     replay_history_device(eng, wl, write_values=True)
     st = build_state(wl, layers=tuple(range(c.L)), maxb=wl.max_blocks(steps), fill_bits=dtype_nan_bits(c.dtype))
@@ -331,10 +331,10 @@ def test_decode_matches_contiguous_baseline():
 # --------------------------------------------------------------------------------
 # full-size workloads: sampled outputs, in the bench's launch configuration
 # --------------------------------------------------------------------------------
-def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=None):
+def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=None, grouped=False):
     wl = with_headroom(make_workload(cfg, block_size=block_size), steps)
     c = wl.cfg
-    eng = make_engine(wl, steps=steps, fused=fused)
+    eng = make_engine(wl, steps=steps, fused=fused, grouped=grouped)
     _say(f"config {cfg}: pool {eng.pool.nbytes / 2**30:.1f} GiB, P={wl.P}, S={wl.S}")
     fill_pool_random(eng, wl)
     replay_history_device(eng, wl, write_values=False)
@@ -656,3 +656,97 @@ def test_multi_query_matrix_path_16_rows(G, Hkv, B, dtype, max_q):
     lens = [max_q, 40, 129, 1000, 2500]
     nqs = [max_q, 3, max_q, 1, max_q - 1]
     _mq_case(rng, G, Hkv, B, dtype, lens, nqs)
+
+
+# --------------------------------------------------------------------------------
+# shared prefixes read once (grouped decode)
+# --------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,fused", [(32, True), (32, False), (16, True), (8, True)])
+def test_grouped_config2_prefix_sharing(B, fused):
+    """Config 2's four prefix-sharing sequences form one run; full parity with
+    the oracle over two steps, and the run is really used."""
+    _say(f"grouped config 2 B={B} fused={fused}")
+    wl, eng, st, results = _small_workload_step(2, steps=2, fused=fused, block_size=B, grouped=True)
+    assert eng.max_shared > 0
+    for got, ref, pairs in results:
+        ok, stats = within_tolerance(got, ref)
+        assert ok, stats
+
+
+@pytest.mark.parametrize("cfg,steps", [(5, 2), (6, 3)])
+def test_grouped_full_size_sampled(cfg, steps):
+    _full_size(cfg, steps=steps, layers=[0, 39], seqs_per_layer=8, seed=80 + cfg, grouped=True)
+
+
+@pytest.mark.parametrize("G,B,dtype", [(1, 16, "f16"), (2, 8, "bf16"), (4, 32, "bf16"), (8, 16, "f16")])
+def test_grouped_direct_random_runs(G, B, dtype):
+    """Random runs: sharing groups of 2-5 sequences with their own tails,
+    singletons and unshared neighbours, NaN in every unused slot."""
+    from oracle.sharing import prefix_groups
+    _say(f"grouped direct G={G} B={B} {dtype}")
+    rng = np.random.default_rng(1500 + G + B)
+    Hkv, d = 2, 128
+    Hq = G * Hkv
+    tables, lens = [], []
+    nxt = 0
+    groups = [(3, 300), (1, 0), (2, 40), (5, 1100), (1, 0), (1, 0), (4, 17)]
+    maxb = 0
+    plan = []
+    for size, prefix in groups:
+        pref_blocks = -(-prefix // B) if prefix else 0
+        pref = list(range(nxt, nxt + pref_blocks))
+        nxt += pref_blocks
+        for m in range(size):
+            n = prefix + int(rng.integers(1, 3 * B)) if prefix else int(rng.integers(1, 900))
+            if prefix % B:     # a partially filled shared block is copied before the sequence's own tokens
+                own_from = pref_blocks - 1
+            else:
+                own_from = pref_blocks
+            nb = -(-n // B)
+            t = pref[:own_from] + list(range(nxt, nxt + nb - own_from))
+            nxt += nb - own_from
+            tables.append(t)
+            lens.append(n)
+            maxb = max(maxb, nb)
+    P = nxt + 2
+    perm = rng.permutation(P)
+    S = len(lens)
+    tab = np.full((S, maxb), 10 ** 6, dtype=np.int32)
+    for s_, t in enumerate(tables):
+        tab[s_, :len(t)] = perm[np.array(t)]
+    from paged_kv_cache_239_amd import Pool
+    pool = Pool(1, Hkv, d, B, P, dtype)
+    K = normal_bits(rng, (1, P, Hkv, B, d), dtype)
+    V = normal_bits(rng, (1, P, Hkv, B, d), dtype)
+    live = np.zeros((P, B), dtype=bool)
+    for s_ in range(S):
+        for t in range(lens[s_]):
+            live[tab[s_, t // B], t % B] = True
+    dead = np.broadcast_to(~live[:, None, :], (P, Hkv, B))
+    K[0][dead] = dtype_nan_bits(dtype)
+    V[0][dead] = dtype_nan_bits(dtype)
+    pool.slab(0, "k").view(torch.int16).copy_(torch.from_numpy(K[0].view(np.int16)))
+    pool.slab(0, "v").view(torch.int16).copy_(torch.from_numpy(V[0].view(np.int16)))
+    host = HostPool.from_arrays(K, V)
+    gs, gl, sg, mg, ms = pool.prefix_groups(tab, np.array(lens, dtype=np.int32))
+    o_gs, o_gl, o_sg = prefix_groups(tab.tolist(), lens, B)
+    assert gs.tolist() == o_gs and gl.tolist() == o_gl and sg.tolist() == o_sg
+    assert ms > 0
+    q = round_to_dtype_bits(rng.standard_normal((S, Hq, d)).astype(np.float32), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    max_ctx = max(lens)
+    max_suffix = int(max(n - gl[g] for n, g in zip(lens, sg)))
+    ws = torch.empty(pool.grouped_workspace_bytes(S, Hq, max_ctx, len(gl), mg, ms, max_suffix), dtype=torch.uint8,
+                     device="cuda")
+    dq = to_device_bits(q, dtype)
+    out = torch.full_like(dq, float("nan"))
+    pool.decode_attention_grouped(0, out, dq, torch.from_numpy(tab).cuda(),
+                                  torch.tensor(lens, dtype=torch.int32, device="cuda"), max_ctx,
+                                  torch.from_numpy(gs).cuda(), torch.from_numpy(gl).cuda(), torch.from_numpy(sg).cuda(),
+                                  mg, ms, max_suffix, scale, ws)
+    torch.cuda.synchronize()
+    got = to_host_f64(out, dtype)
+    ref = decode_layer(host, 0, q, tab, lens, scale, dtype)
+    ok, st = within_tolerance(got, ref)
+    _say(f"stats {st}")
+    assert ok, st
