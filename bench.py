@@ -135,8 +135,12 @@ def write_bytes(S, Hkv, d, b=2) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 100; for a workload of several decode steps, its own "
+                         "steps after the first)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before (default: 5; 1 -- the fork step -- for a workload of "
+                         "several decode steps)")
     ap.add_argument("--config", type=int, default=3, help="workload id (3 = the GQA 32/8 workload)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="store the workload in blocks of this many tokens (8, 16, 32, 64 or 128; "
@@ -189,7 +193,10 @@ def main() -> int:
     if args.queries:
         return multi_query_bench(args)
 
-    W, K = args.warmup, args.steps
+    from workloads import get_config
+    steps_of = get_config(args.config).steps
+    W = args.warmup if args.warmup is not None else (1 if steps_of > 1 else 5)
+    K = args.steps if args.steps is not None else (steps_of - W if steps_of > 1 else 100)
     wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
     c = wl.cfg
     grouped = args.grouped == "on" or (args.grouped == "auto" and c.length_kind == "lognormal_branches")
@@ -430,7 +437,9 @@ def multi_query_bench(args) -> int:
     from paged_kv_cache_239_amd.engine import DecodeEngine
     from workloads import make_workload, with_headroom
 
-    Q, W, K = args.queries, args.warmup, args.steps
+    Q = args.queries
+    W = args.warmup if args.warmup is not None else 1
+    K = args.steps if args.steps is not None else 6
     wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), (W + K) * Q + 1)
     c = wl.cfg
     maxb = wl.max_blocks((W + K) * Q + 1)

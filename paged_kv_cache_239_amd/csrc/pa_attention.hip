@@ -212,6 +212,23 @@ struct Scores {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// (M, L, A) := the eq. (4) combination of (M, L, A) and the partial (m, l, acc)
+__device__ __forceinline__ void fold_partial(float& M, float& L, float (&A)[8], const float* ml, const float* acc) {
+  const float2 x = *reinterpret_cast<const float2*>(ml);
+  if (x.x == -INFINITY) return;
+  const float4 a0 = *reinterpret_cast<const float4*>(acc);
+  const float4 a1 = *reinterpret_cast<const float4*>(acc + 4);
+  const float Mn = fmaxf(M, x.x);
+  const float fo = (M == -INFINITY) ? 0.0f : exp2_fast(M - Mn);
+  const float fn = exp2_fast(x.x - Mn);
+  L = fo * L + fn * x.y;
+  A[0] = fo * A[0] + fn * a0.x; A[1] = fo * A[1] + fn * a0.y;
+  A[2] = fo * A[2] + fn * a0.z; A[3] = fo * A[3] + fn * a0.w;
+  A[4] = fo * A[4] + fn * a1.x; A[5] = fo * A[5] + fn * a1.y;
+  A[6] = fo * A[6] + fn * a1.z; A[7] = fo * A[7] + fn * a1.w;
+  M = Mn;
+}
+
 // shared positions of group g as every pass of the grouped decode reads them
 __device__ __forceinline__ int shared_positions(const int32_t* grp_len, int ngroups, int max_shared, int g) {
   if (g < 0 || g >= ngroups) return 0;
@@ -245,6 +262,7 @@ struct DecodeArgs {
   float* gws_ml = nullptr;  // group pass partials [ngroups][gntiles][Hkv][gparts_max][16][2]
   float* gws_acc = nullptr; // [ngroups][gntiles][Hkv][gparts_max][16][d]
   int gpart_tokens = 1, gparts_max = 1, gntiles = 0;
+  int fold = 0;             // suffix pass: every suffix is one partition, so fold the group partials in here
   const uint4* knew;        // [S][Hkv][d] this step's keys (fused cache write) or null
   const uint4* vnew;        // [S][Hkv][d] this step's values, or null
   const int64_t* slots;     // [S] their slots, or null
@@ -254,6 +272,23 @@ struct DecodeArgs {
   int pstride;              // partitions per (sequence, head) in grid order 1
   float scale_log2;         // softmax scale * log2(e)
 };
+
+// the group-pass partials of sequence s (query head wh of key/value head kvh)
+// folded into (M, L, A): the partitions of its group's L shared positions
+template <int G>
+__device__ __forceinline__ void fold_group_partials(const DecodeArgs& a, int s, int g, int L, int kvh, int wh, int wc,
+                                                    float& M, float& Lsum, float (&A)[8]) {
+  if (L <= 0) return;
+  const int first = min(max(a.q_start[g], 0), a.S);
+  const int w = s - first;
+  const int r = w * G + wh;                     // row among the group's rows
+  const int tile = r / 16, row = r % 16;
+  if (w < 0 || tile >= a.gntiles) return;
+  const int np = (L + a.gpart_tokens - 1) / a.gpart_tokens;
+  const size_t base = (((size_t)g * a.gntiles + tile) * a.Hkv + kvh) * (size_t)a.gparts_max;
+  for (int pp = 0; pp < np; ++pp)
+    fold_partial(M, Lsum, A, a.gws_ml + ((base + pp) * 16 + row) * 2, a.gws_acc + ((base + pp) * 16 + row) * kD + 8 * wc);
+}
 
 #ifdef PA_WAVES_PER_EU
 #define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
@@ -318,11 +353,12 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   // query group and this lane's block-table entry (index clamped into the
   // table row; an entry past the sequence is never used).
   int start = 0;   // first position of this pass (the suffix pass starts after the shared prefix)
+  int grp = -1;
   if constexpr (SUF) {
     int n0 = a.lens[s];
     n0 = n0 < 0 ? 0 : (n0 > a.max_ctx ? a.max_ctx : n0);
-    start = __builtin_amdgcn_readfirstlane(
-        min(shared_positions(a.grp_len, a.ngroups, a.max_shared, a.seq_group[s]), n0));
+    grp = __builtin_amdgcn_readfirstlane(a.seq_group[s]);
+    start = __builtin_amdgcn_readfirstlane(min(shared_positions(a.grp_len, a.ngroups, a.max_shared, grp), n0));
   }
   const int t_begin = start + p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
@@ -690,6 +726,21 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     live = worker && tq < nq;
   }
   uint4* out_row = reinterpret_cast<uint4*>(a.out + orow * kD) + wc;
+  if constexpr (SUF) {
+    if (a.fold) {
+      // one suffix partition: add the group's shared-prefix partials (the
+      // group pass finished one launch earlier) and store the result
+      if (worker) {
+        fold_group_partials<G>(a, s, grp, start, kvh, wh, wc, M, Lsum, A);
+        const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = A[i] * inv;
+        *out_row = narrow8<BF16>(o);
+      }
+      return;
+    }
+  }
   if (!SUF && nparts == 1) {
     if (live) {
       const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
@@ -806,39 +857,12 @@ __global__ __launch_bounds__(G * 16) void cascade_merge_kernel(const DecodeArgs 
   float Mg = -INFINITY, Lg = 0.0f, Ag[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) Ag[i] = 0.0f;
-  auto add = [&](const float* ml, const float* acc) {
-    const float2 x = *reinterpret_cast<const float2*>(ml);
-    if (x.x == -INFINITY) return;
-    const float4 a0 = *reinterpret_cast<const float4*>(acc);
-    const float4 a1 = *reinterpret_cast<const float4*>(acc + 4);
-    const float M = fmaxf(Mg, x.x);
-    const float fo = (Mg == -INFINITY) ? 0.0f : exp2_fast(Mg - M);
-    const float fn = exp2_fast(x.x - M);
-    Lg = fo * Lg + fn * x.y;
-    Ag[0] = fo * Ag[0] + fn * a0.x; Ag[1] = fo * Ag[1] + fn * a0.y;
-    Ag[2] = fo * Ag[2] + fn * a0.z; Ag[3] = fo * Ag[3] + fn * a0.w;
-    Ag[4] = fo * Ag[4] + fn * a1.x; Ag[5] = fo * Ag[5] + fn * a1.y;
-    Ag[6] = fo * Ag[6] + fn * a1.z; Ag[7] = fo * Ag[7] + fn * a1.w;
-    Mg = M;
-  };
-  if (L > 0) {
-    // the group pass wrote this sequence's rows as query token (member) w
-    const int first = min(max(a.q_start[g], 0), a.S);
-    const int w = s - first;
-    const int r = w * G + wh;                     // row among the group's rows
-    const int tile = r / 16, row = r % 16;
-    if (w >= 0 && tile < a.gntiles) {
-      const int np = (L + a.gpart_tokens - 1) / a.gpart_tokens;
-      const size_t base = (((size_t)g * a.gntiles + tile) * a.Hkv + kvh) * (size_t)a.gparts_max;
-      for (int pp = 0; pp < np; ++pp)
-        add(a.gws_ml + ((base + pp) * 16 + row) * 2, a.gws_acc + ((base + pp) * 16 + row) * kD + 8 * wc);
-    }
-  }
+  fold_group_partials<G>(a, s, g, L, kvh, wh, wc, Mg, Lg, Ag);
   if (n > L) {
     const int np = (n - L + a.part_tokens - 1) / a.part_tokens;
     const size_t base = ((size_t)s * a.Hkv + kvh) * (size_t)a.nparts_max;
     for (int pp = 0; pp < np; ++pp)
-      add(a.ws_ml + ((base + pp) * G + wh) * 2, a.ws_acc + ((base + pp) * G + wh) * kD + 8 * wc);
+      fold_partial(Mg, Lg, Ag, a.ws_ml + ((base + pp) * G + wh) * 2, a.ws_acc + ((base + pp) * G + wh) * kD + 8 * wc);
   }
   const float inv = Lg > 0.0f ? 1.0f / Lg : 0.0f;
   float o[8];
@@ -1155,7 +1179,7 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
     }
     return;
   }
-  if (worker) {
+  if (live) {   // rows past the last query hold nothing anyone reads
     const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
     float4* dst = reinterpret_cast<float4*>(a.ws_acc + ((pbase + p) * R + wh) * kD + 8 * wc);
     dst[0] = make_float4(A[0], A[1], A[2], A[3]);
@@ -1672,7 +1696,7 @@ void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3
   constexpr int NWS = suffix_waves(G);
   static_assert(NWS * 64 >= G * 16, "the decode kernel needs G * 16 threads");
   hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa);
-  hipLaunchKernelGGL((cascade_merge_kernel<BF16, G>), dim3(ma.Hkv, ma.S), dim3(G * 16), 0, stream, ma);
+  if (!sa.fold) hipLaunchKernelGGL((cascade_merge_kernel<BF16, G>), dim3(ma.Hkv, ma.S), dim3(G * 16), 0, stream, ma);
 }
 
 template <bool BF16, int BS>
@@ -1777,6 +1801,7 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
                            ? (uint64_t)pool->Hkv * ngroups * wl.gntiles * wl.gcfg.nparts_max : 0;
   // suffix pass (with this step's cache write, if given)
   DecodeArgs sa = args;
+  sa.fold = wl.scfg.nparts_max <= 1 ? 1 : 0;   // every suffix fits one partition: no merge launch
   sa.knew = static_cast<const uint4*>(k_new);
   sa.vnew = static_cast<const uint4*>(v_new);
   sa.slots = slot_mapping;
