@@ -47,6 +47,7 @@
 //     partials visible across the chip's L2 caches without a device-scope
 //     fence per workgroup (such a fence writes back a whole L2).
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -876,11 +877,14 @@ __global__ __launch_bounds__(G * 16) void cascade_merge_kernel(const DecodeArgs 
 //
 // A workgroup's 16 rows are QT = 16 / GQ query tokens x GQ query heads of one
 // key/value head.  Lane = (row = lane % 16, quarter kq = lane / 16).  Per
-// 16-token step of a wave:
+// 16-token step of a wave the key and value tiles are loaded as whole
+// 256-byte rows (lane: tokens 4j + kq, dims 8 row .. +7; each instruction
+// reads 1 KiB contiguous) into per-wave LDS tiles, then
 //   S^T[token][row] = K[token][:] . Q[row][:]   4 x mfma 16x16x32: A = the
-//       key tile as loaded (lane: token `row`, dims 32ks + 8kq .. +7), B = Q^T
-//       held in registers (lane: query row `row`, the same dims); the result
-//       gives lane (row, kq) the scores of tokens 4kq .. 4kq+3 for its row;
+//       key tile read back row-major (lane: token `row`, dims 32ks + 8kq ..
+//       +7; 272-byte rows), B = Q^T held in registers (lane: query row
+//       `row`, the same dims); the result gives lane (row, kq) the scores of
+//       tokens 4kq .. 4kq+3 for its row;
 //   O^T[dim][row] += V^T[dim][token] . P^T[token][row]   8 x mfma 16x16x16:
 //       B = the lane's own four probabilities (the layout S^T came out in),
 //       A = V^T, read from a per-wave LDS copy of the value tile (token t
@@ -918,6 +922,8 @@ __device__ __forceinline__ f32x4_t mfma_k16(const uint2 a, const uint2 b, f32x4_
 }
 
 constexpr int kVRow = 288;   // bytes per token row of the LDS value tile (256 + 32 pad)
+constexpr int kKRow = 272;   // bytes per token row of an LDS key tile (256 + 16 pad)
+
 
 // GRP: the group pass of the grouped decode -- "sequence" s is group s, its
 // query tokens are the group's sequences (one query each), every row sees the
@@ -995,6 +1001,7 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
 
   // value tiles during the loop; the cross-wave combine reuses the space
   __shared__ __attribute__((aligned(16))) char s_v[NW][2][16 * kVRow];
+  __shared__ __attribute__((aligned(16))) char s_k[NW][2][16 * kKRow];
   static_assert(sizeof(s_v) >= sizeof(float) * NW * R * kD, "combine buffer must fit");
   float (*s_acc)[R][kD] = reinterpret_cast<float (*)[R][kD]>(&s_v[0][0][0]);
   __shared__ float s_m[NW][R];
@@ -1007,25 +1014,27 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // lane loads token `row` of the step, dims 32ks + 8kq .. +7, of K and V
+  // lane loads tokens 4j + kq of the step, dims 8 row .. +7: each load
+  // instruction reads four whole 256-byte rows
   auto load_group = [&](int k, uint4 (&K)[4], uint4 (&V)[4], bool tail) {
     const int g = g_first + k * NW;
-    const int tok = g * 16 + row;
-    int phys = __builtin_amdgcn_readlane(my_phys[0], k);
-    if constexpr (BPG == 2) {
-      const int phys1 = __builtin_amdgcn_readlane(my_phys[1], k);
-      phys = row < 8 ? phys : phys1;
-    }
-    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + kq * 16;
-    const bool ok = !tail || tok < n;
+    const int tok0 = g * 16;
+    uint64_t base[BPG];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ok) {
-        K[ks] = nt_load16(a.kslab + off + ks * 64);
-        V[ks] = nt_load16(a.vslab + off + ks * 64);
+    for (int b = 0; b < BPG; ++b)
+      base[b] = (uint64_t)__builtin_amdgcn_readlane(my_phys[b], k) * a.tile_bytes + head_off + row * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * j + kq;                        // token of the step
+      const int b = BPG == 2 ? j / 2 : 0;              // its block when BS = 8
+      const int rib = BS >= 16 ? tok0 % BS + t : t % BS;
+      const uint64_t off = base[b] + (uint64_t)rib * kRowBytes;
+      if (!tail || tok0 + t < n) {
+        K[j] = nt_load16(a.kslab + off);
+        V[j] = nt_load16(a.vslab + off);
       } else {
-        K[ks] = make_uint4(0, 0, 0, 0);
-        V[ks] = make_uint4(0, 0, 0, 0);
+        K[j] = make_uint4(0, 0, 0, 0);
+        V[j] = make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -1034,16 +1043,24 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
   auto process_group = [&](int g, const uint4 (&K)[4], const uint4 (&V)[4], bool tail) {
     const int tok0 = g * 16;
     char* vb = s_v[wave][buf];
+    char* kb = s_k[wave][buf];
     buf ^= 1;
-    {
-      const int vrow = (row & 3) * 4 + (row >> 2);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<uint4*>(vb + vrow * kVRow + (32 * ks + 8 * kq) * 2) = V[ks];
+    for (int j = 0; j < 4; ++j) {
+      // token t = 4j + kq: key row t, value row (t % 4) * 4 + t / 4 = kq * 4 + j
+      *reinterpret_cast<uint4*>(kb + (4 * j + kq) * kKRow + row * 16) = K[j];
+      *reinterpret_cast<uint4*>(vb + (kq * 4 + j) * kVRow + row * 16) = V[j];
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st = mfma_k32<BF16>(K[ks], qb[ks], st);
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 kx = *reinterpret_cast<const uint4*>(kb + row * kKRow + (32 * ks + 8 * kq) * 2);
+      st = mfma_k32<BF16>(kx, qb[ks], st);
+    }
+
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -1144,13 +1161,12 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
   }
   __syncthreads();
 
-  const int t = threadIdx.x;
-  const bool worker = t < R * 16;
-  const int wh = t >> 4;
-  const int wc = t & 15;
-  float A[8];
-  float M = -INFINITY, Lsum = 0.0f;
-  if (worker) {
+  // one thread per (row, 8-dim chunk); fewer than 4 waves loop over them
+  for (int t = threadIdx.x; t < R * 16; t += NW * 64) {
+    const int wh = t >> 4;
+    const int wc = t & 15;
+    float A[8];
+    float M = -INFINITY, Lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][wh]);
 #pragma unroll
@@ -1165,21 +1181,17 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
       A[0] += wt * a0.x; A[1] += wt * a0.y; A[2] += wt * a0.z; A[3] += wt * a0.w;
       A[4] += wt * a1.x; A[5] += wt * a1.y; A[6] += wt * a1.z; A[7] += wt * a1.w;
     }
-  }
-  const int otq = tile * QT + wh / GQ;
-  const bool live = worker && otq < nq;
-  const size_t orow = (size_t)(q0 + (otq < nq ? otq : 0)) * a.Hq + (size_t)kvh * GQ + wh % GQ;
-  if (!GRP && nparts == 1) {
-    if (live) {
+    const int otq = tile * QT + wh / GQ;
+    if (otq >= nq) continue;   // rows past the last query hold nothing anyone reads
+    if (!GRP && nparts == 1) {
+      const size_t orow = (size_t)(q0 + otq) * a.Hq + (size_t)kvh * GQ + wh % GQ;
       const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
       float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = A[i] * inv;
       *(reinterpret_cast<uint4*>(a.out + orow * kD) + wc) = narrow8<BF16>(o);
+      continue;
     }
-    return;
-  }
-  if (live) {   // rows past the last query hold nothing anyone reads
     const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
     float4* dst = reinterpret_cast<float4*>(a.ws_acc + ((pbase + p) * R + wh) * kD + 8 * wc);
     dst[0] = make_float4(A[0], A[1], A[2], A[3]);
@@ -1195,8 +1207,6 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
 // from there: K as the A operand read back row-major (272-byte stride:
 // conflict-free 16-byte reads), V transposed as in mq_mfma_kernel.  A wave
 // finishes its rows alone; no cross-wave combine.
-constexpr int kKRow = 272;   // bytes per token row of the LDS key tile (256 + 16 pad)
-
 template <bool BF16, int GQ, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs a) {
   constexpr int R = 16 * NW;        // rows per workgroup
@@ -1660,6 +1670,13 @@ struct GroupedLayout {
   size_t g_ml = 0, g_acc = 0, s_ml = 0, s_acc = 0, total = 0;
 };
 
+// The group pass runs two-wave workgroups: shared prompts are short, and
+// with four waves each would get only a few steps.
+#ifndef PA_GROUP_WAVES
+#define PA_GROUP_WAVES 2
+#endif
+constexpr int kGroupWaves = PA_GROUP_WAVES;
+
 // The suffix pass runs one-wave workgroups (two for G = 8: the kernel stages
 // the query and combines with G * 16 threads): suffixes are short (the tail
 // of a prompt's last block plus the tokens generated since the fork).
@@ -1674,6 +1691,8 @@ GroupedLayout grouped_layout(int S, int Hkv, int G, int max_suffix, int ngroups,
     w.gcfg.part_tokens = 16 * kWaves;
   } else {
     w.gcfg = choose_launch(ngroups * w.gntiles, Hkv, max_shared);
+    // a lane of a group-pass wave holds the block of one of its steps
+    w.gcfg.part_tokens = std::min(w.gcfg.part_tokens, 16 * 64 * kGroupWaves);
   }
   w.scfg.part_tokens = kSuffixPart;
   w.gcfg.nparts_max = max_shared > 0 ? (max_shared + w.gcfg.part_tokens - 1) / w.gcfg.part_tokens : 1;
@@ -1692,7 +1711,7 @@ template <bool BF16, int G, int BS>
 void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3 sgrid, const DecodeArgs& ma,
                     hipStream_t stream) {
   if (ggrid.x > 0)
-    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kWaves, true>), ggrid, dim3(kWaves * 64), 0, stream, ga);
+    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kGroupWaves, true>), ggrid, dim3(kGroupWaves * 64), 0, stream, ga);
   constexpr int NWS = suffix_waves(G);
   static_assert(NWS * 64 >= G * 16, "the decode kernel needs G * 16 threads");
   hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa);
