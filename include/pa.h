@@ -26,6 +26,15 @@
  *    grouped-query attention has fewer key/value heads than query heads.
  *    Query head h reads key/value head floor(h / G), G = Hq / Hkv.
  *
+ * Beyond the decode step (each declared below with its source):
+ *  - beam selection as forks and frees (pa_seq_reorder);
+ *  - preemption by swapping a group of sequences to a host pool and back
+ *    (pa_move_blocks, pa_swap_blocks);
+ *  - several causal queries per sequence, for chunked prefill and
+ *    speculative verification (pa_multi_query_attention);
+ *  - decode that reads a prefix shared by parallel samples or beams once
+ *    per group (pa_prefix_groups, pa_decode_attention_grouped).
+ *
  * Conventions for every call:
  *  - Return value: PA_OK (0) or a negative pa_status.  No call aborts or
  *    throws across the ABI.  After a failure, pa_last_error() returns a
