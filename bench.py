@@ -145,6 +145,9 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=0,
                     help="store the workload in blocks of this many tokens (8, 16, 32, 64 or 128; "
                          "default: the workload's own)")
+    ap.add_argument("--head-shards", type=int, default=1, metavar="N",
+                    help="run one GPU's share of the workload when its heads are split over N GPUs "
+                         "(Hq / N and Hkv / N heads, same sequences)")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="instead of decode steps: swap the first N sequences of the workload out to a "
                          "pinned host pool and back, and time it")
@@ -197,7 +200,8 @@ def main() -> int:
     steps_of = get_config(args.config).steps
     W = args.warmup if args.warmup is not None else (1 if steps_of > 1 else 5)
     K = args.steps if args.steps is not None else (steps_of - W if steps_of > 1 else 100)
-    wl = with_headroom(make_workload(args.config, block_size=args.block_size or None), W + K + 1)
+    wl = with_headroom(make_workload(args.config, block_size=args.block_size or None,
+                                     head_shards=args.head_shards), W + K + 1)
     c = wl.cfg
     grouped = args.grouped == "on" or (args.grouped == "auto" and c.length_kind == "lognormal_branches")
     eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(W + K),

@@ -1425,7 +1425,11 @@ struct LaunchCfg {
 };
 
 // Partition length: as long as possible (fewer partials to merge) while the
-// grid still has several workgroups per compute unit.
+// grid still has several workgroups per compute unit.  With long contexts a
+// partition keeps at least 6 steps per wave (384 tokens): shorter ones spend
+// more in start-up and in the merge than the extra workgroups gain (one
+// key/value head over 64 sequences of 512-4096 tokens: 64-token partitions
+// take 1.8x as long per layer as 384-token ones).
 LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
   static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
   int gpw = 12;
@@ -1433,7 +1437,8 @@ LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
     gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
   } else {
     const int64_t target = 2048;  // workgroups: 256 CUs x 8
-    while (gpw > 1) {
+    const int floor_gpw = max_ctx >= 2 * 16 * kWaves * 6 ? 6 : 1;
+    while (gpw > floor_gpw) {
       const int64_t part = 16LL * kWaves * gpw;
       const int64_t wgs = (int64_t)S * Hkv * ((max_ctx + part - 1) / part);
       if (wgs >= target) break;

@@ -331,8 +331,9 @@ def test_decode_matches_contiguous_baseline():
 # --------------------------------------------------------------------------------
 # full-size workloads: sampled outputs, in the bench's launch configuration
 # --------------------------------------------------------------------------------
-def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=None, grouped=False):
-    wl = with_headroom(make_workload(cfg, block_size=block_size), steps)
+def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=None, grouped=False,
+               head_shards=1):
+    wl = with_headroom(make_workload(cfg, block_size=block_size, head_shards=head_shards), steps)
     c = wl.cfg
     eng = make_engine(wl, steps=steps, fused=fused, grouped=grouped)
     _say(f"config {cfg}: pool {eng.pool.nbytes / 2**30:.1f} GiB, P={wl.P}, S={wl.S}")
@@ -397,6 +398,14 @@ def test_config6_beam_search_sampled():
 def test_config3_other_block_sizes_sampled(B):
     """The config-3 batch stored in blocks of B tokens (block-size sweep)."""
     _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=4, seed=60 + B, block_size=B)
+
+
+@pytest.mark.parametrize("shards", [2, 8])
+def test_config3_head_shard_sampled(shards):
+    """One GPU's share of the config-3 heads when they are split over
+    `shards` GPUs (8 shards: 4 query heads over 1 key/value head): a smaller
+    grid, so shorter partitions and more of them per sequence."""
+    _full_size(3, steps=2, layers=[0, 31], seqs_per_layer=6, seed=70 + shards, head_shards=shards)
 
 
 @pytest.mark.parametrize("cfg", [1, 2])

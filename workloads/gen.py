@@ -245,13 +245,25 @@ def _at_block_size(c: DecodeConfig, B: int, lengths0: np.ndarray) -> DecodeConfi
     return dataclasses.replace(c, **kw)
 
 
-def make_workload(cfg_id: int, block_size: int | None = None) -> Workload:
+def _head_shard(c: DecodeConfig, n: int) -> DecodeConfig:
+    """One GPU's share of ``c`` when its heads are split over ``n`` GPUs:
+    Hq / n query heads and Hkv / n key/value heads (a query group stays with
+    its key/value head); sequences, lengths, history and seeds unchanged."""
+    if n < 1 or c.Hkv % n:
+        raise ValueError(f"{n} shards do not divide {c.Hkv} key/value heads")
+    return dataclasses.replace(c, Hq=c.Hq // n, Hkv=c.Hkv // n, name=f"{c.name}_heads1of{n}")
+
+
+def make_workload(cfg_id: int, block_size: int | None = None, head_shards: int = 1) -> Workload:
     """Workload ``cfg_id``; ``block_size`` runs the same sequences, history and
-    values over blocks of another size."""
+    values over blocks of another size; ``head_shards`` > 1 keeps one GPU's
+    share of the heads."""
     c = get_config(cfg_id)
     lengths0 = _lengths(c)
     if block_size is not None and int(block_size) != c.B:
         c = _at_block_size(c, int(block_size), lengths0)
+    if int(head_shards) != 1:
+        c = _head_shard(c, int(head_shards))
     assert lengths0.shape[0] == c.S
     P = _pool_blocks(c, lengths0)
     perm = rng_for(c.cfg_id, 0, P_PERM).permutation(P).astype(np.int32)
