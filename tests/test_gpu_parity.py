@@ -431,16 +431,18 @@ def test_small_workloads_at_every_block_size(cfg):
         del eng
 
 
-@pytest.mark.parametrize("cfg,steps", [(1, 2), (2, 2), (5, 1), (6, 2)])
-def test_fused_write_attention_equals_separate_calls(cfg, steps):
-    """pa_write_kv_decode_attention == pa_write_kv then pa_decode_attention:
+@pytest.mark.parametrize("cfg,steps,grouped", [(1, 2, False), (2, 2, False), (5, 1, False), (6, 2, False),
+                                               (5, 1, True), (6, 2, True)])
+def test_fused_write_attention_equals_separate_calls(cfg, steps, grouped):
+    """pa_write_kv_decode_attention == pa_write_kv then pa_decode_attention
+    (grouped: pa_decode_attention_grouped with and without the cache write):
     outputs and the whole pool byte for byte."""
-    _say(f"fused vs separate, config {cfg}")
+    _say(f"fused vs separate, config {cfg} grouped={grouped}")
     wl = make_workload(cfg)
     c = wl.cfg
     engines = []
     for fused in (True, False):
-        eng = make_engine(wl, steps=steps, fused=fused)
+        eng = make_engine(wl, steps=steps, fused=fused, grouped=grouped)
         if cfg in (5, 6):
             fill_pool_random(eng, wl)
             replay_history_device(eng, wl, write_values=False)
@@ -687,13 +689,17 @@ def test_grouped_full_size_sampled(cfg, steps):
     _full_size(cfg, steps=steps, layers=[0, 39], seqs_per_layer=8, seed=80 + cfg, grouped=True)
 
 
+@pytest.mark.parametrize("short", [False, True])
 @pytest.mark.parametrize("G,B,dtype", [(1, 16, "f16"), (2, 8, "bf16"), (4, 32, "bf16"), (8, 16, "f16")])
-def test_grouped_direct_random_runs(G, B, dtype):
+def test_grouped_direct_random_runs(G, B, dtype, short):
     """Random runs: sharing groups of 2-5 sequences with their own tails,
-    singletons and unshared neighbours, NaN in every unused slot."""
+    singletons and unshared neighbours, NaN in every unused slot.  With
+    `short`, no sequence has more than 128 positions beyond its run's shared
+    prefix (members' tails and unshared sequences alike), as in a few steps
+    of sampling after a fork."""
     from oracle.sharing import prefix_groups
-    _say(f"grouped direct G={G} B={B} {dtype}")
-    rng = np.random.default_rng(1500 + G + B)
+    _say(f"grouped direct G={G} B={B} {dtype} short={short}")
+    rng = np.random.default_rng(1500 + G + B + (7 if short else 0))
     Hkv, d = 2, 128
     Hq = G * Hkv
     tables, lens = [], []
@@ -706,7 +712,10 @@ def test_grouped_direct_random_runs(G, B, dtype):
         pref = list(range(nxt, nxt + pref_blocks))
         nxt += pref_blocks
         for m in range(size):
-            n = prefix + int(rng.integers(1, 3 * B)) if prefix else int(rng.integers(1, 900))
+            if short:
+                n = prefix + int(rng.integers(1, min(3 * B, 64))) if prefix else int(rng.integers(1, 100))
+            else:
+                n = prefix + int(rng.integers(1, 3 * B)) if prefix else int(rng.integers(1, 900))
             if prefix % B:     # a partially filled shared block is copied before the sequence's own tokens
                 own_from = pref_blocks - 1
             else:
@@ -745,6 +754,8 @@ def test_grouped_direct_random_runs(G, B, dtype):
     scale = float(np.float32(1 / np.sqrt(d)))
     max_ctx = max(lens)
     max_suffix = int(max(n - gl[g] for n, g in zip(lens, sg)))
+    if short:
+        assert max_suffix <= 128 and ms <= 2048
     ws = torch.empty(pool.grouped_workspace_bytes(S, Hq, max_ctx, len(gl), mg, ms, max_suffix), dtype=torch.uint8,
                      device="cuda")
     dq = to_device_bits(q, dtype)
