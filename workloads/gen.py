@@ -251,7 +251,9 @@ def _head_shard(c: DecodeConfig, n: int) -> DecodeConfig:
     its key/value head); sequences, lengths, history and seeds unchanged."""
     if n < 1 or c.Hkv % n:
         raise ValueError(f"{n} shards do not divide {c.Hkv} key/value heads")
-    return dataclasses.replace(c, Hq=c.Hq // n, Hkv=c.Hkv // n, name=f"{c.name}_heads1of{n}")
+    return dataclasses.replace(c, Hq=c.Hq // n, Hkv=c.Hkv // n, name=f"{c.name}_heads1of{n}",
+                               description=f"{c.description}; one GPU's share with the heads split over {n} "
+                                           f"GPUs: {c.Hq // n} query / {c.Hkv // n} KV heads")
 
 
 def make_workload(cfg_id: int, block_size: int | None = None, head_shards: int = 1) -> Workload:
