@@ -104,26 +104,30 @@ __device__ __forceinline__ void widen8(const uint4 v, float (&f)[8]) {
   }
 }
 
-// float -> 16-bit storage pattern, round to nearest even
+// float -> fp16 bit pattern, round to nearest even
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// two floats -> two 16-bit patterns (a in the low half), round to nearest
+// even; bf16 through the packed hardware conversion (one instruction)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <bool BF16>
-__device__ __forceinline__ uint32_t narrow1(float x) {
-  if constexpr (BF16) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-  } else {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
-  }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+  else
+    return f16_bits(a) | (f16_bits(b) << 16);
 }
 
 template <bool BF16>
 __device__ __forceinline__ uint4 narrow8(const float (&f)[8]) {
   uint4 r;
-  r.x = narrow1<BF16>(f[0]) | (narrow1<BF16>(f[1]) << 16);
-  r.y = narrow1<BF16>(f[2]) | (narrow1<BF16>(f[3]) << 16);
-  r.z = narrow1<BF16>(f[4]) | (narrow1<BF16>(f[5]) << 16);
-  r.w = narrow1<BF16>(f[6]) | (narrow1<BF16>(f[7]) << 16);
+  r.x = pack2<BF16>(f[0], f[1]);
+  r.y = pack2<BF16>(f[2], f[3]);
+  r.z = pack2<BF16>(f[4], f[5]);
+  r.w = pack2<BF16>(f[6], f[7]);
   return r;
 }
 
@@ -1088,19 +1092,12 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
     // probabilities as the MFMA's 16-bit operand; bf16 keeps 8 significant
     // bits, so there the remainder goes in a second product (error ~2^-17)
     uint2 pb, pl = make_uint2(0, 0);
-    {
-      uint32_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = narrow1<BF16>(pe[i]);
-      pb.x = h[0] | (h[1] << 16);
-      pb.y = h[2] | (h[3] << 16);
-      if constexpr (BF16) {
-        uint32_t r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = narrow1<true>(pe[i] - __builtin_bit_cast(float, h[i] << 16));
-        pl.x = r[0] | (r[1] << 16);
-        pl.y = r[2] | (r[3] << 16);
-      }
+    pb.x = pack2<BF16>(pe[0], pe[1]);
+    pb.y = pack2<BF16>(pe[2], pe[3]);
+    if constexpr (BF16) {
+      // what the rounding left out: p - bf16(p), itself rounded to bf16
+      pl.x = pack2<true>(pe[0] - __builtin_bit_cast(float, pb.x << 16), pe[1] - __builtin_bit_cast(float, pb.x & 0xffff0000u));
+      pl.y = pack2<true>(pe[2] - __builtin_bit_cast(float, pb.y << 16), pe[3] - __builtin_bit_cast(float, pb.y & 0xffff0000u));
     }
     // the value tile written above by all lanes of the wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1208,7 +1205,8 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
 // conflict-free 16-byte reads), V transposed as in mq_mfma_kernel.  A wave
 // finishes its rows alone; no cross-wave combine.
 template <bool BF16, int GQ, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void mq_mfma_rows_kernel(
+    const DecodeArgs a) {
   constexpr int R = 16 * NW;        // rows per workgroup
   constexpr int QT = R / GQ;        // query tokens per workgroup
   static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
@@ -1271,8 +1269,10 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs 
     if (lane < nsteps) my_phys[b] = entry[b] < 0 ? 0 : (entry[b] >= a.P ? a.P - 1 : entry[b]);
   }
 
-  __shared__ __attribute__((aligned(16))) char s_k[2][16 * kKRow];
-  __shared__ __attribute__((aligned(16))) char s_v[2][16 * kVRow];
+  // three tile buffers: step k's values, step k+1's keys (scored ahead) and
+  // step k+2 (being stored) are all live during step k
+  __shared__ __attribute__((aligned(16))) char s_k[3][16 * kKRow];
+  __shared__ __attribute__((aligned(16))) char s_v[3][16 * kVRow];
 
   // this thread's share of a step: token lt = tid / 16, 16 bytes at dims 8 lc
   const int lt = tid >> 4;
@@ -1305,21 +1305,37 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs 
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint4 Kn, Vn;
-  load_step(0, Kn, Vn);
-  store_step(0, Kn, Vn);
-  if (nsteps > 1) load_step(1, Kn, Vn);
-  __syncthreads();
-  for (int k = 0; k < nsteps; ++k) {
-    const int b = k & 1;
-    const int tok0 = (step0 + k) * 16;
-    // scores: A = K[token row][dims 32ks + 8kq ..] from LDS, B = Q^T
+  // scores of the step in buffer bb: A = K[token row][dims 32ks + 8kq ..]
+  // from LDS, B = Q^T
+  auto scores = [&](int bb) {
     f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 kx = *reinterpret_cast<const uint4*>(s_k[b] + row * kKRow + (32 * ks + 8 * kq) * 2);
+      const uint4 kx = *reinterpret_cast<const uint4*>(s_k[bb] + row * kKRow + (32 * ks + 8 * kq) * 2);
       st = mfma_k32<BF16>(kx, qb[ks], st);
     }
+    return st;
+  };
+
+  // Software pipeline: step k+1's score products are issued before step k's
+  // softmax, so the matrix cores work while the vector units do.
+  uint4 Kn, Vn;
+  load_step(0, Kn, Vn);
+  store_step(0, Kn, Vn);
+  if (nsteps > 1) {
+    load_step(1, Kn, Vn);
+    store_step(1, Kn, Vn);
+  }
+  if (nsteps > 2) load_step(2, Kn, Vn);
+  __syncthreads();
+  f32x4_t st = scores(0);
+  int b = 0;   // buffer of step k; k + 1 is in b1, k + 2 goes to b2
+  for (int k = 0; k < nsteps; ++k) {
+    const int b1 = b == 2 ? 0 : b + 1;
+    const int b2 = b1 == 2 ? 0 : b1 + 1;
+    const int tok0 = (step0 + k) * 16;
+    f32x4_t st_next = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (k + 1 < nsteps) st_next = scores(b1);
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -1345,19 +1361,12 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs 
       ell += pe[i];
     }
     uint2 pb, pl = make_uint2(0, 0);
-    {
-      uint32_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = narrow1<BF16>(pe[i]);
-      pb.x = h[0] | (h[1] << 16);
-      pb.y = h[2] | (h[3] << 16);
-      if constexpr (BF16) {
-        uint32_t r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = narrow1<true>(pe[i] - __builtin_bit_cast(float, h[i] << 16));
-        pl.x = r[0] | (r[1] << 16);
-        pl.y = r[2] | (r[3] << 16);
-      }
+    pb.x = pack2<BF16>(pe[0], pe[1]);
+    pb.y = pack2<BF16>(pe[2], pe[3]);
+    if constexpr (BF16) {
+      // what the rounding left out: p - bf16(p), itself rounded to bf16
+      pl.x = pack2<true>(pe[0] - __builtin_bit_cast(float, pb.x << 16), pe[1] - __builtin_bit_cast(float, pb.x & 0xffff0000u));
+      pl.y = pack2<true>(pe[2] - __builtin_bit_cast(float, pb.y << 16), pe[3] - __builtin_bit_cast(float, pb.y & 0xffff0000u));
     }
     const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[b]);
 #pragma unroll
@@ -1369,13 +1378,16 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs 
       acc[nb] = mfma_k16<BF16>(va, pb, acc[nb]);
       if constexpr (BF16) acc[nb] = mfma_k16<BF16>(va, pl, acc[nb]);
     }
-    // next step's tiles into the other buffer; the barrier also closes this
-    // step's reads before the buffer is written again
-    if (k + 1 < nsteps) {
-      store_step(b ^ 1, Kn, Vn);
-      if (k + 2 < nsteps) load_step(k + 2, Kn, Vn);
+    // step k+2's tiles into the buffer step k-1 left (every wave finished
+    // with it before the last barrier); the barrier below publishes them and
+    // closes this step's reads of buffer b before step k+3 overwrites it
+    if (k + 2 < nsteps) {
+      store_step(b2, Kn, Vn);
+      if (k + 3 < nsteps) load_step(k + 3, Kn, Vn);
     }
     __syncthreads();
+    st = st_next;
+    b = b1;
   }
 
   // ---- this wave's 16 rows: sum the four quarters, then store ---------------
@@ -1389,8 +1401,8 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_rows_kernel(const DecodeArgs 
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         uint2 w;
-        w.x = narrow1<BF16>(acc[nb][0] * inv) | (narrow1<BF16>(acc[nb][1] * inv) << 16);
-        w.y = narrow1<BF16>(acc[nb][2] * inv) | (narrow1<BF16>(acc[nb][3] * inv) << 16);
+        w.x = pack2<BF16>(acc[nb][0] * inv, acc[nb][1] * inv);
+        w.y = pack2<BF16>(acc[nb][2] * inv, acc[nb][3] * inv);
         *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * kq) = w;
       }
     }
