@@ -157,6 +157,9 @@ def main() -> int:
     ap.add_argument("--grouped", choices=["auto", "on", "off"], default="auto",
                     help="read prefixes that several sequences share once per group (auto: for the "
                          "workloads whose sequences share prompt blocks)")
+    ap.add_argument("--order", choices=["on", "off"], default="on",
+                    help="launch the context partitions longest first from the manager's lengths "
+                         "(pa_decode_attention_ordered); off: the fixed grid order")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--dump", default="", help="write per-step and per-launch times (JSON) here")
@@ -205,7 +208,7 @@ def main() -> int:
     c = wl.cfg
     grouped = args.grouped == "on" or (args.grouped == "auto" and c.length_kind == "lognormal_branches")
     eng = DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(W + K),
-                       free_order=wl.free_order, grouped=grouped)
+                       free_order=wl.free_order, grouped=grouped, ordered=args.order == "on")
     # seeded N(0,1) pool contents (device RNG), then the prefill history on the native manager
     for layer in range(c.L):
         for which in ("k", "v"):

@@ -345,6 +345,40 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k,
                                        float scale, void* workspace,
                                        size_t ws_bytes, hipStream_t stream);
 
+/* pa_decode_attention (k, v, slot_mapping all NULL) or
+ * pa_write_kv_decode_attention (all three given) with the context
+ * partitions launched longest first.  The same attention as those calls
+ * ("vLLM PagedAttention and continuous batching", sections "PagedAttention:
+ * fixed blocks, non-contiguous physical memory" and "The kernel page"); the
+ * difference is only the order of the work.  The host's block manager
+ * knows every sequence's length, so the library lists exactly the
+ * partitions that hold positions: all full partitions first, then each
+ * sequence's last, shorter one from the longest to the shortest.  No
+ * workgroup is launched past a sequence's end, and the ones that start last
+ * are short.
+ *   host_context_lens : host int32 [S], equal to what context_lens holds
+ *                       when the launch executes (the manager's copy);
+ *                       read during the call only.  A value that differs
+ *                       gives wrong outputs for that sequence but no access
+ *                       outside the arguments.
+ * Other arguments, results and errors as for pa_write_kv_decode_attention
+ * (k, v: device [S][Hkv][d]; slot_mapping: device int64 [S]) and
+ * pa_decode_attention; the same workspace.  INVALID_ARG if only some of k,
+ * v and slot_mapping are given, or host_context_lens is NULL while S > 0.
+ * Outputs are bitwise those of the unordered calls.  Launches whose
+ * partitions do not fit one list (over 512 (sequence, partition) units)
+ * run in the fixed order. */
+pa_status pa_decode_attention_ordered(pa_pool* pool, int layer, const void* k,
+                                      const void* v,
+                                      const int64_t* slot_mapping, void* out,
+                                      const void* q, int S, int Hq,
+                                      const int32_t* block_tables, int maxb,
+                                      const int32_t* context_lens,
+                                      const int32_t* host_context_lens,
+                                      int max_ctx, float scale,
+                                      void* workspace, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* Several query tokens per sequence over the same block tables: chunked
  * prefill ("vLLM PagedAttention and continuous batching", section "Chunked
  * prefill": a prefill that does not fit the step's budget is split, each

@@ -46,10 +46,20 @@
 //     (sequence, head) by the eq. (4) rescale.  The kernel boundary makes the
 //     partials visible across the chip's L2 caches without a device-scope
 //     fence per workgroup (such a fence writes back a whole L2).
+//   * Launch order.  Given host copies of the context lengths (the block
+//     manager holds them), the host lists the (sequence, partition) units
+//     longest first -- every full partition, then each sequence's shorter
+//     last one from the longest to the shortest -- and passes the list in
+//     the kernel arguments.  Workgroups start in id order, so the device
+//     stays full until the short units at the end, and no workgroup is
+//     launched past a sequence's end.  Without host lengths the grid gives
+//     every sequence max_ctx's partition count, and the surplus workgroups
+//     exit after reading the length.
 
 #include <algorithm>
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "pa_device_common.h"
 
@@ -295,6 +305,16 @@ __device__ __forceinline__ void fold_group_partials(const DecodeArgs& a, int s, 
     fold_partial(M, Lsum, A, a.gws_ml + ((base + pp) * 16 + row) * 2, a.gws_acc + ((base + pp) * 16 + row) * kD + 8 * wc);
 }
 
+// Longest-first order of a decode launch, built on the host from host
+// copies of the context lengths: unit u = (sequence << 12) | partition, and
+// workgroup id = u * Hkv + head.  Passed by value (kernel arguments), so a
+// workgroup finds its partition with one scalar load and the grid holds
+// exactly the partitions that have work.
+constexpr int kMaxUnits = 512;
+constexpr int kUnitPartBits = 12;
+template <bool ON> struct UnitList { int unused; };
+template <> struct UnitList<true> { int count; uint32_t unit[kMaxUnits]; };
+
 #ifdef PA_WAVES_PER_EU
 #define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
 #else
@@ -309,8 +329,12 @@ __device__ __forceinline__ void fold_group_partials(const DecodeArgs& a, int s, 
 // SUF: the suffix pass of the grouped decode -- sequence s attends only to
 // its own positions from the end of its group's shared prefix, and always
 // leaves partials for the cascade merge.
-template <bool BF16, int G, int BS, int NW, int QT, bool SUF = false>
-__global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a) {
+// SCHED (one query per sequence): the workgroup's (sequence, partition)
+// comes from the unit list instead of the fixed grid order.
+template <bool BF16, int G, int BS, int NW, int QT, bool SUF = false, bool SCHED = false>
+__global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a,
+                                                                                const UnitList<SCHED> ul) {
+  static_assert(!SCHED || (QT == 0 && !SUF), "unit lists order single-query decode launches");
   using SC = Scores<G>;
   constexpr int GQ = QT > 0 ? G / QT : G;
   static_assert(QT == 0 || GQ * QT == G, "rows = query tokens x query heads");
@@ -330,7 +354,13 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   int kvh, s, p, tile = 0;
   {
     const uint32_t id = blockIdx.x;
-    if (QT > 0) {                      // head, then query tile, sequence, partition
+    if constexpr (SCHED) {
+      kvh = id % a.Hkv;
+      const uint32_t w = ul.unit[min(id / a.Hkv, (uint32_t)kMaxUnits - 1)];
+      s = (int)(w >> kUnitPartBits);
+      p = (int)(w & ((1u << kUnitPartBits) - 1));
+      if (s >= a.S) return;
+    } else if (QT > 0) {                      // head, then query tile, sequence, partition
       kvh = id % a.Hkv;
       uint32_t t = id / a.Hkv;
       tile = t % a.ntiles;
@@ -1442,9 +1472,13 @@ struct LaunchCfg {
 // more in start-up and in the merge than the extra workgroups gain (one
 // key/value head over 64 sequences of 512-4096 tokens: 64-token partitions
 // take 1.8x as long per layer as 384-token ones).
-LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
+// Launches in longest-first order (unit lists) start from 16 steps per
+// wave: with no workgroup past a sequence's end and the short partitions
+// last, longer partitions only save start-up (config-3 batch: 99-100 us per
+// layer at 12-32 steps per wave, 103-105 at 6-8).
+LaunchCfg choose_launch(int S, int Hkv, int max_ctx, bool ordered = false) {
   static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
-  int gpw = 12;
+  int gpw = ordered ? 16 : 12;
   if (forced > 0) {
     gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
   } else {
@@ -1454,7 +1488,7 @@ LaunchCfg choose_launch(int S, int Hkv, int max_ctx) {
       const int64_t part = 16LL * kWaves * gpw;
       const int64_t wgs = (int64_t)S * Hkv * ((max_ctx + part - 1) / part);
       if (wgs >= target) break;
-      gpw /= 2;
+      gpw = std::max(gpw / 2, floor_gpw);
     }
   }
   LaunchCfg cfg;
@@ -1481,10 +1515,63 @@ WsLayout ws_layout(int S, int Hkv, int G, const LaunchCfg& cfg) {
 
 template <bool BF16, int G, int BS, int QT>
 void launch_decode(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves, QT>), grid, dim3(kWaves * 64), 0, stream, args);
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves, QT>), grid, dim3(kWaves * 64), 0, stream, args,
+                     UnitList<false>{});
   if (args.nparts_max > 1)
     hipLaunchKernelGGL((decode_merge_kernel<BF16, G, QT>), dim3(args.Hkv, args.S, args.ntiles), dim3(G * 16), 0,
                        stream, args);
+}
+
+template <bool BF16, int G, int BS>
+void launch_decode_ordered(const DecodeArgs& args, const UnitList<true>& ul, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, kWaves, 0, false, true>),
+                     dim3((unsigned)(ul.count * args.Hkv)), dim3(kWaves * 64), 0, stream, args, ul);
+  if (args.nparts_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, G, 0>), dim3(args.Hkv, args.S, 1), dim3(G * 16), 0, stream, args);
+}
+
+template <bool BF16, int BS>
+bool dispatch_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_decode_ordered<BF16, 1, BS>(args, ul, stream); return true;
+    case 2: launch_decode_ordered<BF16, 2, BS>(args, ul, stream); return true;
+    case 4: launch_decode_ordered<BF16, 4, BS>(args, ul, stream); return true;
+    case 8: launch_decode_ordered<BF16, 8, BS>(args, ul, stream); return true;
+    default: return false;
+  }
+}
+
+// The units of a decode launch, longest first: every full partition
+// (partition-major), then each sequence's last, shorter partition from the
+// longest to the shortest (an empty sequence is one unit of length 0).  The
+// workgroups that start last are then the short ones, so the launch ends
+// soon after the device stops being full.  Returns the count, or -1 when
+// they do not fit one list.
+int order_units(const int32_t* host_lens, int S, int max_ctx, int part, UnitList<true>& ul) {
+  std::vector<int> full(S);
+  std::vector<std::pair<int, int>> rest;   // (length of the last partition, sequence)
+  int maxf = 0;
+  int64_t count = 0;
+  for (int s = 0; s < S; ++s) {
+    const int n = std::min(std::max(host_lens[s], 0), max_ctx);
+    full[s] = n / part;
+    const int r = n % part;
+    if (r > 0 || n == 0) rest.emplace_back(r, s);
+    maxf = std::max(maxf, full[s]);
+    count += full[s];
+  }
+  count += (int64_t)rest.size();
+  if (count > kMaxUnits || maxf >= (1 << kUnitPartBits)) return -1;
+  int c = 0;
+  for (int p = 0; p < maxf; ++p)
+    for (int s = 0; s < S; ++s)
+      if (p < full[s]) ul.unit[c++] = ((uint32_t)s << kUnitPartBits) | (uint32_t)p;
+  std::stable_sort(rest.begin(), rest.end(), [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
+    return x.first > y.first;
+  });
+  for (const auto& rs : rest) ul.unit[c++] = ((uint32_t)rs.second << kUnitPartBits) | (uint32_t)full[rs.second];
+  ul.count = c;
+  return c;
 }
 
 // G query heads per key/value head.  One query per sequence: the rows of a
@@ -1577,7 +1664,8 @@ namespace {
 pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int S, int Hq,
                         const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx, float scale,
                         void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
-                        const int64_t* slot_mapping, const int32_t* q_start, int T, int max_q, hipStream_t stream) {
+                        const int64_t* slot_mapping, const int32_t* q_start, int T, int max_q, hipStream_t stream,
+                        const int32_t* host_lens = nullptr) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
   if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
@@ -1608,7 +1696,7 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const int ntiles = plan.ntiles;
   const int rows = multi ? plan.rows : G;
 
-  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx);
+  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, !multi && host_lens != nullptr);
   if (multi && plan.wide && cfg.part_tokens > kWidePartMax) {
     cfg.part_tokens = kWidePartMax;
     cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
@@ -1655,6 +1743,20 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
+  if (!multi && host_lens != nullptr) {
+    static thread_local UnitList<true> ul;
+    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0) {
+      switch (pool->B) {
+        case 8: ok = bf16 ? dispatch_ordered<true, 8>(G, args, ul, stream) : dispatch_ordered<false, 8>(G, args, ul, stream); break;
+        case 16: ok = bf16 ? dispatch_ordered<true, 16>(G, args, ul, stream) : dispatch_ordered<false, 16>(G, args, ul, stream); break;
+        case 32: ok = bf16 ? dispatch_ordered<true, 32>(G, args, ul, stream) : dispatch_ordered<false, 32>(G, args, ul, stream); break;
+        case 64: ok = bf16 ? dispatch_ordered<true, 64>(G, args, ul, stream) : dispatch_ordered<false, 64>(G, args, ul, stream); break;
+        default: ok = bf16 ? dispatch_ordered<true, 128>(G, args, ul, stream) : dispatch_ordered<false, 128>(G, args, ul, stream); break;
+      }
+      if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+      return hip_check(hipGetLastError(), "decode attention launch");
+    }
+  }
   if (multi && plan.mfma) {
     switch (pool->B) {
       case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 8>(G, plan.wide, args, grid, stream); break;
@@ -1731,7 +1833,8 @@ void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3
     hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kGroupWaves, true>), ggrid, dim3(kGroupWaves * 64), 0, stream, ga);
   constexpr int NWS = suffix_waves(G);
   static_assert(NWS * 64 >= G * 16, "the decode kernel needs G * 16 threads");
-  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa);
+  hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa,
+                     UnitList<false>{});
   if (!sa.fold) hipLaunchKernelGGL((cascade_merge_kernel<BF16, G>), dim3(ma.Hkv, ma.S), dim3(G * 16), 0, stream, ma);
 }
 
@@ -1898,6 +2001,24 @@ pa_status pa_decode_attention(pa_pool* pool, int layer, void* out, const void* q
   pa_detail::clear_error();
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
                        ws_bytes, nullptr, nullptr, nullptr, nullptr, 0, 0, stream);
+}
+
+pa_status pa_decode_attention_ordered(pa_pool* pool, int layer, const void* k, const void* v,
+                                      const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+                                      const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                      const int32_t* host_context_lens, int max_ctx, float scale, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (S > 0 && !host_context_lens) return fail(PA_ERR_INVALID_ARG, "NULL host_context_lens");
+  const bool fused = k != nullptr || v != nullptr || slot_mapping != nullptr;
+  if (S > 0 && fused) {
+    if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "k, v and slot_mapping must all be given or all NULL");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
+  }
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
+                       ws_bytes, fused ? k : nullptr, fused ? v : nullptr, fused ? slot_mapping : nullptr, nullptr, 0,
+                       0, stream, host_context_lens);
 }
 
 size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx, int max_q) {

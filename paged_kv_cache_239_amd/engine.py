@@ -58,10 +58,13 @@ class _Staging:
 class DecodeEngine:
     def __init__(self, L: int, Hq: int, Hkv: int, d: int, B: int, P: int, dtype: str, S: int, maxb: int,
                  free_order: Optional[Sequence[int]] = None, device: str = "cuda", fused: bool = True,
-                 grouped: bool = False):
+                 grouped: bool = False, ordered: bool = True):
         import torch
         self.torch = torch
         self.fused = fused
+        # launch the context partitions longest first from the manager's own
+        # lengths (pa_decode_attention_ordered)
+        self.ordered = ordered
         self.grouped = grouped
         self.L, self.Hq, self.Hkv, self.d, self.B, self.P = L, Hq, Hkv, d, B, P
         self.S, self.maxb = S, maxb
@@ -222,6 +225,12 @@ class DecodeEngine:
                     self.d_group_start[: self.n_groups + 1], self.d_group_len[: self.n_groups], self.d_seq_group,
                     self.max_group, self.max_shared, self.max_suffix, scale, self.gws,
                     k=knews[layer] if fused else None, v=vnews[layer] if fused else None,
+                    slot_mapping=self.d_slots if fused else None, stream=stream)
+            elif self.ordered:
+                fused = self.fused
+                self.pool.decode_attention_ordered(
+                    layer, outs[layer], qs[layer], self.d_tables, self.d_lens, self.lens, max_ctx, scale,
+                    workspace=self.ws, k=knews[layer] if fused else None, v=vnews[layer] if fused else None,
                     slot_mapping=self.d_slots if fused else None, stream=stream)
             elif self.fused:
                 self.pool.write_kv_decode_attention(layer, knews[layer], vnews[layer], self.d_slots, outs[layer],

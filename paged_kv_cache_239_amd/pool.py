@@ -331,6 +331,25 @@ class Pool:
             _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), C.c_float(scale),
             C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
 
+    def decode_attention_ordered(self, layer: int, out, q, block_tables, context_lens, host_context_lens,
+                                 max_ctx: int, scale: float, workspace=None, k=None, v=None, slot_mapping=None,
+                                 stream=None) -> None:
+        """decode_attention (or, with k, v and slot_mapping, the fused
+        write_kv_decode_attention) with the context partitions launched
+        longest first; ``host_context_lens`` is a host int32 array equal to
+        ``context_lens`` (see pa_decode_attention_ordered)."""
+        S, Hq = int(q.shape[0]), int(q.shape[1])
+        maxb = int(block_tables.shape[1])
+        hl = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+        if hl.shape != (S,):
+            raise ValueError("host_context_lens must hold one length per sequence")
+        ws_ptr, ws_bytes = (0, 0) if workspace is None else (_ptr(workspace), int(workspace.numel()))
+        opt = (lambda t: None if t is None else C.c_void_p(_ptr(t)))
+        check(self.lib, self.lib.pa_decode_attention_ordered(
+            self.handle, layer, opt(k), opt(v), opt(slot_mapping), _ptr(out), _ptr(q), S, Hq,
+            _ptr(block_tables), maxb, _ptr(context_lens), hl.ctypes.data, int(max_ctx), C.c_float(scale),
+            C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
+
 
 def multi_query_workspace(pool: Pool, S: int, Hq: int, max_ctx: int, max_q: int, device="cuda", stream=None):
     """A zero-initialised workspace for ``pool.multi_query_attention``."""

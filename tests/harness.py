@@ -70,11 +70,12 @@ def to_host_bits(t) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def make_engine(wl, steps: int = 1, device="cuda", fused: bool = True, grouped: bool = False):
+def make_engine(wl, steps: int = 1, device="cuda", fused: bool = True, grouped: bool = False,
+                ordered: bool = True):
     from paged_kv_cache_239_amd.engine import DecodeEngine
     c = wl.cfg
     return DecodeEngine(c.L, c.Hq, c.Hkv, c.d, c.B, wl.P, c.dtype, wl.S, wl.max_blocks(steps),
-                        free_order=wl.free_order, device=device, fused=fused, grouped=grouped)
+                        free_order=wl.free_order, device=device, fused=fused, grouped=grouped, ordered=ordered)
 
 
 def replay_history_device(eng, wl, write_values: bool) -> None:

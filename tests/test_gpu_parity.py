@@ -314,6 +314,110 @@ def test_decode_bitwise_invariant_under_block_permutation_and_reruns():
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
 
 
+def test_decode_partition_merge_with_garbage_and_reused_workspace():
+    """Every partial the merge reads is written by the same call: a
+    workspace full of garbage (all-ones bytes, which are NaN partials, then
+    random bytes) and a workspace reused by the previous call must both give
+    the oracle's result.  One context of 30,000 tokens spreads over 79
+    partitions."""
+    _say("partition merge: garbage and reused workspace")
+    rng = np.random.default_rng(7)
+    lens = [30000, 777, 5000, 1, 1600, 384, 385, 12345]
+    dtype = "f16"
+    Hkv, G = 2, 4
+    pool, host, tables, q = _direct_case(rng, len(lens), G * Hkv, Hkv, 16, dtype, lens)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    S, Hq = q.shape[0], q.shape[1]
+    max_ctx = max(lens)
+    nbytes = pool.workspace_bytes(S, Hq, max_ctx)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    ref = decode_layer(host, 0, q, tables, lens, scale, dtype)
+    q2 = round_to_dtype_bits(rng.standard_normal(q.shape).astype(np.float32), dtype)
+    ref2 = decode_layer(host, 0, q2, tables, lens, scale, dtype)
+    fills = [("all-ones bytes", lambda: ws.fill_(255)),
+             ("random bytes", lambda: ws.copy_(torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)))),
+             ("reused", lambda: None)]
+    for (name, fill), (qq, rr) in zip(fills, [(q, ref), (q2, ref2), (q, ref)]):
+        fill()
+        dq = to_device_bits(qq, dtype)
+        out = torch.empty_like(dq)
+        pool.decode_attention(0, out, dq, d_tables, d_lens, max_ctx, scale, workspace=ws)
+        torch.cuda.synchronize()
+        ok, stats = within_tolerance(to_host_f64(out, dtype), rr)
+        _say(f"{name}: {stats}")
+        assert ok, (name, stats)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", ["ragged", "many"])
+def test_decode_ordered_equals_fixed_order(fused, case):
+    """Partitions launched longest first from host copies of the lengths
+    give the fixed grid order's outputs (and, fused, its pool) bit for bit,
+    and the oracle's within tolerance: empty sequences, lengths at and
+    around partition multiples.  "many" has more (sequence, partition)
+    units than one list holds and runs in the fixed order."""
+    _say(f"ordered launch {case} fused={fused}")
+    rng = np.random.default_rng(11)
+    dtype, B, Hkv, G = "bf16", 16, 2, 4
+    if case == "ragged":
+        lens = [0, 1, 383, 384, 385, 767, 768, 769, 1536, 2047, 4096, 5000, 12345, 3, 0, 900]
+    else:
+        lens = [int(x) for x in rng.integers(1, 100, size=600)]
+    S, Hq = len(lens), G * Hkv
+    pool, host, tables, q = _direct_case(rng, S, Hq, Hkv, B, dtype, [max(n, 1) for n in lens])
+    scale = float(np.float32(1 / np.sqrt(128)))
+    max_ctx = max(lens)
+    from paged_kv_cache_239_amd import decode_workspace
+    ws = decode_workspace(pool, S, Hq, max_ctx)
+    d_tables = torch.from_numpy(tables).cuda()
+    hl = np.asarray(lens, dtype=np.int32)
+    d_lens = torch.from_numpy(hl).cuda()
+    dq = to_device_bits(q, dtype)
+    knew = normal_bits(rng, (S, Hkv, 128), dtype)
+    vnew = normal_bits(rng, (S, Hkv, 128), dtype)
+    slots = np.array([int(tables[s, (n - 1) // B]) * B + (n - 1) % B if n > 0 else -1
+                      for s, n in enumerate(lens)], dtype=np.int64)
+    dk, dv, ds = to_device_bits(knew, dtype), to_device_bits(vnew, dtype), torch.from_numpy(slots).cuda()
+    out_fixed, out_ord = torch.empty_like(dq), torch.empty_like(dq)
+    if fused:
+        pool.write_kv_decode_attention(0, dk, dv, ds, out_fixed, dq, d_tables, d_lens, max_ctx, scale, workspace=ws)
+        torch.cuda.synchronize()
+        pool_fixed = to_host_bits(pool.buffer).copy()
+        pool.decode_attention_ordered(0, out_ord, dq, d_tables, d_lens, hl, max_ctx, scale, workspace=ws,
+                                      k=dk, v=dv, slot_mapping=ds)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(pool.buffer), pool_fixed)
+        write_kv(host, 0, knew, vnew, [int(x) for x in slots])
+    else:
+        pool.decode_attention(0, out_fixed, dq, d_tables, d_lens, max_ctx, scale, workspace=ws)
+        pool.decode_attention_ordered(0, out_ord, dq, d_tables, d_lens, hl, max_ctx, scale, workspace=ws)
+        torch.cuda.synchronize()
+    assert torch.equal(out_fixed.view(torch.int16), out_ord.view(torch.int16))
+    got = to_host_f64(out_ord, dtype)
+    live = [s for s, n in enumerate(lens) if n > 0]
+    assert np.all(got[[s for s, n in enumerate(lens) if n == 0]] == 0)
+    ref = decode_layer(host, 0, q[live], tables[live], [lens[s] for s in live], scale, dtype)
+    ok, stats = within_tolerance(got[live], ref)
+    _say(f"stats {stats}")
+    assert ok, stats
+
+
+def test_decode_ordered_rejects_partial_fused_arguments():
+    rng = np.random.default_rng(12)
+    pool, host, tables, q = _direct_case(rng, 2, 4, 2, 16, "f16", [10, 20])
+    from paged_kv_cache_239_amd import PAError
+    dq = to_device_bits(q, "f16")
+    out = torch.empty_like(dq)
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.tensor([10, 20], dtype=torch.int32, device="cuda")
+    k = torch.zeros((2, 2, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(PAError):
+        pool.decode_attention_ordered(0, out, dq, d_tables, d_lens, np.array([10, 20], np.int32), 20, 0.1, k=k)
+
+
 def test_decode_matches_contiguous_baseline():
     """Paged result vs the oracle's dense attention on contiguous K/V."""
     _say("contiguous baseline")
