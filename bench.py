@@ -417,7 +417,10 @@ def main() -> int:
                                       "(unique bytes); the logical figures count it once per sequence, "
                                       "and may exceed the HBM peak since repeated reads hit in cache")
     rec = recorded_traffic()
-    if rec is not None and (c.dtype, c.G, c.B) == ("bf16", 4, 16):
+    # counters apply only to the workload and launch mode they were taken on
+    here = {"config": args.config, "block_size": c.B, "head_shards": args.head_shards or 1,
+            "order": args.order, "grouped": bool(grouped)}
+    if rec is not None and rec.get("workload") == here:
         result["roofline"]["traffic"] = int(rec["traffic_bytes_per_launch"])
         result["roofline"]["traffic_note"] = (
             f"rocprofv3 FETCH_SIZE x{rec['fetch_scale']} + WRITE_SIZE x{rec['write_scale']} per launch "
