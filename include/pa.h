@@ -352,10 +352,10 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k,
  * fixed blocks, non-contiguous physical memory" and "The kernel page"); the
  * difference is only the order of the work.  The host's block manager
  * knows every sequence's length, so the library lists exactly the
- * partitions that hold positions: all full partitions first, then each
- * sequence's last, shorter one from the longest to the shortest.  No
- * workgroup is launched past a sequence's end, and the ones that start last
- * are short.
+ * partitions that hold positions, longest first.  A sequence's partitions
+ * share its length equally (no short remainder partitions).  No workgroup
+ * is launched past a sequence's end, and the ones that start last are the
+ * shortest.
  *   host_context_lens : host int32 [S], equal to what context_lens holds
  *                       when the launch executes (the manager's copy);
  *                       read during the call only.  A value that differs
@@ -365,9 +365,11 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k,
  * (k, v: device [S][Hkv][d]; slot_mapping: device int64 [S]) and
  * pa_decode_attention; the same workspace.  INVALID_ARG if only some of k,
  * v and slot_mapping are given, or host_context_lens is NULL while S > 0.
- * Outputs are bitwise those of the unordered calls.  Launches whose
+ * The partition boundaries differ from the unordered calls', so outputs
+ * agree with theirs within rounding, not bitwise; for given inputs they
+ * are deterministic and the same at every block size.  Launches whose
  * partitions do not fit one list (over 512 (sequence, partition) units)
- * run in the fixed order. */
+ * run as the unordered calls do. */
 pa_status pa_decode_attention_ordered(pa_pool* pool, int layer, const void* k,
                                       const void* v,
                                       const int64_t* slot_mapping, void* out,

@@ -47,14 +47,14 @@
 //     partials visible across the chip's L2 caches without a device-scope
 //     fence per workgroup (such a fence writes back a whole L2).
 //   * Launch order.  Given host copies of the context lengths (the block
-//     manager holds them), the host lists the (sequence, partition) units
-//     longest first -- every full partition, then each sequence's shorter
-//     last one from the longest to the shortest -- and passes the list in
-//     the kernel arguments.  Workgroups start in id order, so the device
-//     stays full until the short units at the end, and no workgroup is
-//     launched past a sequence's end.  Without host lengths the grid gives
-//     every sequence max_ctx's partition count, and the surplus workgroups
-//     exit after reading the length.
+//     manager holds them), the host splits each sequence into partitions of
+//     equal length, lists the (sequence, partition) units longest first and
+//     passes the list in the kernel arguments.  Workgroups start in id
+//     order, so the device stays full until the shortest units at the end,
+//     and no workgroup is launched past a sequence's end.  Without host
+//     lengths every partition but a sequence's last has part_tokens
+//     positions, the grid gives every sequence max_ctx's partition count,
+//     and the surplus workgroups exit after reading the length.
 
 #include <algorithm>
 #include <cmath>
@@ -283,6 +283,7 @@ struct DecodeArgs {
   const int64_t* slots;     // [S] their slots, or null
   int64_t nslots;           // P * B
   int S, Hq, Hkv, P, maxb, max_ctx, part_tokens, nparts_max;
+  int equal_chunks = 0;     // unit lists: a sequence's partitions share its length equally
   int grid_order;           // see decode_attention_kernel
   int pstride;              // partitions per (sequence, head) in grid order 1
   float scale_log2;         // softmax scale * log2(e)
@@ -306,12 +307,12 @@ __device__ __forceinline__ void fold_group_partials(const DecodeArgs& a, int s, 
 }
 
 // Longest-first order of a decode launch, built on the host from host
-// copies of the context lengths: unit u = (sequence << 12) | partition, and
-// workgroup id = u * Hkv + head.  Passed by value (kernel arguments), so a
-// workgroup finds its partition with one scalar load and the grid holds
-// exactly the partitions that have work.
+// copies of the context lengths: unit u = (sequence << 16) | (first
+// position / 16), and workgroup id = u * Hkv + head.  Passed by value
+// (kernel arguments), so a workgroup finds its partition with one scalar
+// load and the grid holds exactly the partitions that have work.
 constexpr int kMaxUnits = 512;
-constexpr int kUnitPartBits = 12;
+constexpr int kUnitStepBits = 16;
 template <bool ON> struct UnitList { int unused; };
 template <> struct UnitList<true> { int count; uint32_t unit[kMaxUnits]; };
 
@@ -357,8 +358,8 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     if constexpr (SCHED) {
       kvh = id % a.Hkv;
       const uint32_t w = ul.unit[min(id / a.Hkv, (uint32_t)kMaxUnits - 1)];
-      s = (int)(w >> kUnitPartBits);
-      p = (int)(w & ((1u << kUnitPartBits) - 1));
+      s = (int)(w >> kUnitStepBits);
+      p = (int)(w & ((1u << kUnitStepBits) - 1));   // first 16-token step; the partition index follows from n
       if (s >= a.S) return;
     } else if (QT > 0) {                      // head, then query tile, sequence, partition
       kvh = id % a.Hkv;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     grp = __builtin_amdgcn_readfirstlane(a.seq_group[s]);
     start = __builtin_amdgcn_readfirstlane(min(shared_positions(a.grp_len, a.ngroups, a.max_shared, grp), n0));
   }
-  const int t_begin = start + p * a.part_tokens;
+  const int t_begin = SCHED ? p * 16 : start + p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
   const int32_t* table = a.tables + (size_t)s * a.maxb;
   uint4 qv = make_uint4(0, 0, 0, 0);
@@ -435,8 +436,16 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   n = __builtin_amdgcn_readfirstlane(n);
   const int nparts = SUF ? (n - start + a.part_tokens - 1) / a.part_tokens
                          : (n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1);
+  // Partition length: part_tokens, or with equal chunks the sequence's
+  // nparts partitions share its length (rounded up to 16 tokens).
+  int plen = a.part_tokens;
+  if constexpr (SCHED) {
+    if (a.equal_chunks && nparts > 1) plen = ((n + nparts - 1) / nparts + 15) & ~15;
+    if (t_begin % plen) return;   // not a partition start of this length
+    p = t_begin / plen;
+  }
   if (p >= nparts) return;
-  const int t_end = min(n, t_begin + a.part_tokens);
+  const int t_end = min(n, t_begin + plen);
 
   __shared__ uint4 s_q[G * 16];
   __shared__ __attribute__((aligned(16))) float s_p[NW][2][4][4 * G];
@@ -1472,13 +1481,16 @@ struct LaunchCfg {
 // more in start-up and in the merge than the extra workgroups gain (one
 // key/value head over 64 sequences of 512-4096 tokens: 64-token partitions
 // take 1.8x as long per layer as 384-token ones).
-// Launches in longest-first order (unit lists) start from 16 steps per
-// wave: with no workgroup past a sequence's end and the short partitions
-// last, longer partitions only save start-up (config-3 batch: 99-100 us per
-// layer at 12-32 steps per wave, 103-105 at 6-8).
+// Launches in longest-first order (unit lists) split each sequence into
+// ceil(n / part) partitions of equal length and start from 24 steps per
+// wave (1,536 tokens).  A workgroup is latency-bound: its first loads wait
+// for two memory round trips, so a short partition moves its bytes at a
+// fraction of a full one's rate; equal partitions have no short remainders
+// (config-3 batch: 98 us per layer, against 100-101 with full partitions
+// plus a remainder at 16-24 steps per wave, and 103-105 at 6-8).
 LaunchCfg choose_launch(int S, int Hkv, int max_ctx, bool ordered = false) {
   static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
-  int gpw = ordered ? 16 : 12;
+  int gpw = ordered ? 24 : 12;
   if (forced > 0) {
     gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
   } else {
@@ -1541,35 +1553,29 @@ bool dispatch_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, h
   }
 }
 
-// The units of a decode launch, longest first: every full partition
-// (partition-major), then each sequence's last, shorter partition from the
-// longest to the shortest (an empty sequence is one unit of length 0).  The
-// workgroups that start last are then the short ones, so the launch ends
-// soon after the device stops being full.  Returns the count, or -1 when
-// they do not fit one list.
-int order_units(const int32_t* host_lens, int S, int max_ctx, int part, UnitList<true>& ul) {
-  std::vector<int> full(S);
-  std::vector<std::pair<int, int>> rest;   // (length of the last partition, sequence)
-  int maxf = 0;
-  int64_t count = 0;
+// The units of a decode launch, longest first.  With `equal` a sequence
+// of n positions gets np = ceil(n / part) partitions of equal length
+// (ceil(n / np) rounded up to 16; the last may be shorter by the rounding),
+// otherwise full partitions of `part` and a shorter last one.  An empty
+// sequence is one unit of length 0 (it writes zeros).  Workgroups start in
+// id order, so the device stays full until the shortest units, which start
+// last.  Returns the count, or -1 when they do not fit one list.
+int order_units(const int32_t* host_lens, int S, int max_ctx, int part, bool equal, UnitList<true>& ul) {
+  struct U { int len, s, step; };
+  std::vector<U> units;
   for (int s = 0; s < S; ++s) {
     const int n = std::min(std::max(host_lens[s], 0), max_ctx);
-    full[s] = n / part;
-    const int r = n % part;
-    if (r > 0 || n == 0) rest.emplace_back(r, s);
-    maxf = std::max(maxf, full[s]);
-    count += full[s];
+    const int np = n > 0 ? (n + part - 1) / part : 1;
+    const int plen = (equal && np > 1) ? ((n + np - 1) / np + 15) / 16 * 16 : part;
+    if ((int64_t)n > ((int64_t)1 << kUnitStepBits) * 16 - plen) return -1;
+    for (int p = 0; p < np; ++p) {
+      units.push_back({std::max(std::min(plen, n - p * plen), 0), s, p * plen / 16});
+      if ((int)units.size() > kMaxUnits) return -1;
+    }
   }
-  count += (int64_t)rest.size();
-  if (count > kMaxUnits || maxf >= (1 << kUnitPartBits)) return -1;
+  std::stable_sort(units.begin(), units.end(), [](const U& x, const U& y) { return x.len > y.len; });
   int c = 0;
-  for (int p = 0; p < maxf; ++p)
-    for (int s = 0; s < S; ++s)
-      if (p < full[s]) ul.unit[c++] = ((uint32_t)s << kUnitPartBits) | (uint32_t)p;
-  std::stable_sort(rest.begin(), rest.end(), [](const std::pair<int, int>& x, const std::pair<int, int>& y) {
-    return x.first > y.first;
-  });
-  for (const auto& rs : rest) ul.unit[c++] = ((uint32_t)rs.second << kUnitPartBits) | (uint32_t)full[rs.second];
+  for (const U& u : units) ul.unit[c++] = ((uint32_t)u.s << kUnitStepBits) | (uint32_t)u.step;
   ul.count = c;
   return c;
 }
@@ -1745,7 +1751,8 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const bool bf16 = pool->dtype == PA_BF16;
   if (!multi && host_lens != nullptr) {
     static thread_local UnitList<true> ul;
-    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0) {
+    args.equal_chunks = 1;
+    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, true, ul) > 0) {
       switch (pool->B) {
         case 8: ok = bf16 ? dispatch_ordered<true, 8>(G, args, ul, stream) : dispatch_ordered<false, 8>(G, args, ul, stream); break;
         case 16: ok = bf16 ? dispatch_ordered<true, 16>(G, args, ul, stream) : dispatch_ordered<false, 16>(G, args, ul, stream); break;

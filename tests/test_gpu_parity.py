@@ -353,12 +353,13 @@ def test_decode_partition_merge_with_garbage_and_reused_workspace():
 
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("case", ["ragged", "many"])
-def test_decode_ordered_equals_fixed_order(fused, case):
-    """Partitions launched longest first from host copies of the lengths
-    give the fixed grid order's outputs (and, fused, its pool) bit for bit,
-    and the oracle's within tolerance: empty sequences, lengths at and
-    around partition multiples.  "many" has more (sequence, partition)
-    units than one list holds and runs in the fixed order."""
+def test_decode_ordered_matches_oracle_and_fixed_order(fused, case):
+    """Partitions of equal length launched longest first from host copies
+    of the lengths: the oracle's outputs within tolerance, the same bits on
+    a rerun, and (fused) the same pool as the fixed grid order; empty
+    sequences, lengths at and around partition multiples.  "many" has more
+    (sequence, partition) units than one list holds and runs as the fixed
+    order does, bit for bit."""
     _say(f"ordered launch {case} fused={fused}")
     rng = np.random.default_rng(11)
     dtype, B, Hkv, G = "bf16", 16, 2, 4
@@ -395,7 +396,19 @@ def test_decode_ordered_equals_fixed_order(fused, case):
         pool.decode_attention(0, out_fixed, dq, d_tables, d_lens, max_ctx, scale, workspace=ws)
         pool.decode_attention_ordered(0, out_ord, dq, d_tables, d_lens, hl, max_ctx, scale, workspace=ws)
         torch.cuda.synchronize()
-    assert torch.equal(out_fixed.view(torch.int16), out_ord.view(torch.int16))
+    again = torch.empty_like(dq)
+    pool.decode_attention_ordered(0, again, dq, d_tables, d_lens, hl, max_ctx, scale, workspace=ws,
+                                  k=dk if fused else None, v=dv if fused else None,
+                                  slot_mapping=ds if fused else None)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out_ord.view(torch.int16))
+    if case == "many":
+        assert torch.equal(out_fixed.view(torch.int16), out_ord.view(torch.int16))
+    for o in (out_fixed, out_ord):
+        assert within_tolerance(to_host_f64(o, dtype)[[s for s, n in enumerate(lens) if n > 0]],
+                                decode_layer(host, 0, q[[s for s, n in enumerate(lens) if n > 0]],
+                                             tables[[s for s, n in enumerate(lens) if n > 0]],
+                                             [n for n in lens if n > 0], scale, dtype))[0]
     got = to_host_f64(out_ord, dtype)
     live = [s for s, n in enumerate(lens) if n > 0]
     assert np.all(got[[s for s, n in enumerate(lens) if n == 0]] == 0)
