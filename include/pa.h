@@ -451,6 +451,31 @@ pa_status pa_decode_attention_grouped(pa_pool* pool, int layer, const void* k,
                                       void* workspace, size_t ws_bytes,
                                       hipStream_t stream);
 
+/* pa_decode_attention_grouped with the group pass launched longest first
+ * (the partition order of pa_decode_attention_ordered, applied to the
+ * prefixes that "vLLM PagedAttention and continuous batching", section
+ * "Sharing with reference counts and copy-on-write", lets parallel samples
+ * and beams share).  Each group's shared positions are split into
+ * partitions of equal length, and only partitions that hold positions are
+ * launched.
+ *   host_group_len : host int32 [n_groups], equal to what group_len holds
+ *                    when the launch executes (pa_prefix_groups' host
+ *                    output); read during the call only.  A value that
+ *                    differs gives wrong outputs for that group's members
+ *                    but no access outside the arguments.
+ * Other arguments, results, errors and workspace as for
+ * pa_decode_attention_grouped; INVALID_ARG if host_group_len is NULL while
+ * n_groups > 0.  Outputs agree with pa_decode_attention_grouped within
+ * rounding (the group partitions differ), and are deterministic. */
+pa_status pa_decode_attention_grouped_ordered(
+    pa_pool* pool, int layer, const void* k, const void* v,
+    const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+    const int32_t* block_tables, int maxb, const int32_t* context_lens,
+    int max_ctx, const int32_t* group_start, const int32_t* group_len,
+    const int32_t* seq_group, const int32_t* host_group_len, int n_groups,
+    int max_group, int max_shared, int max_suffix, float scale,
+    void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes for pa_decode_attention_grouped up to these sizes (never
  * decreasing in any argument); 0 for invalid sizes. */
 size_t pa_decode_grouped_workspace_bytes(const pa_pool* pool, int S, int Hq,

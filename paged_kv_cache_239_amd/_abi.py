@@ -104,6 +104,9 @@ DEVICE_SIGNATURES = {
     "pa_decode_attention_grouped": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P, C.c_int,
                                               P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, P, C.c_size_t,
                                               P]),
+    "pa_decode_attention_grouped_ordered": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P,
+                                                      C.c_int, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int,
+                                                      C.c_float, P, C.c_size_t, P]),
     "pa_decode_grouped_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                                        C.c_int]),
 }

@@ -972,8 +972,9 @@ constexpr int kKRow = 272;   // bytes per token row of an LDS key tile (256 + 16
 // query tokens are the group's sequences (one query each), every row sees the
 // group's shared positions, read through the first member's table, and the
 // result is always left as partials for the cascade merge.
-template <bool BF16, int GQ, int BS, int NW, bool GRP = false>
-__global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
+template <bool BF16, int GQ, int BS, int NW, bool GRP = false, bool SCHED = false>
+__global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, const UnitList<SCHED> ul) {
+  static_assert(!SCHED || GRP, "unit lists order the group pass");
   constexpr int R = 16;             // rows per workgroup
   constexpr int QT = R / GQ;        // query tokens per workgroup
   static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
@@ -986,15 +987,22 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
     uint32_t t = id / a.Hkv;
     tile = t % a.ntiles;
     t /= a.ntiles;
-    s = t % a.S;
-    p = t / a.S;
+    if constexpr (SCHED) {            // unit = (group, first 16-token step), longest first
+      const uint32_t w = ul.unit[min(t, (uint32_t)kMaxUnits - 1)];
+      s = (int)(w >> kUnitStepBits);
+      p = (int)(w & ((1u << kUnitStepBits) - 1));
+      if (s >= a.S) return;
+    } else {
+      s = t % a.S;
+      p = t / a.S;
+    }
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15;
   const int kq = lane >> 4;
 
-  const int t_begin = p * a.part_tokens;
+  const int t_begin = SCHED ? p * 16 : p * a.part_tokens;
   const int g_first = t_begin / 16 + wave;
   const int q0 = min(max(a.q_start[s], 0), a.T);
   int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
@@ -1030,8 +1038,14 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a) {
     n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
   }
   const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
+  int plen = a.part_tokens;
+  if constexpr (SCHED) {              // the group's nparts partitions share its length
+    if (nparts > 1) plen = ((n + nparts - 1) / nparts + 15) & ~15;
+    if (t_begin % plen) return;
+    p = t_begin / plen;
+  }
   if (p >= nparts) return;
-  const int t_end = min(n, t_begin + a.part_tokens);
+  const int t_end = min(n, t_begin + plen);
   const int lim = tq < nq ? (GRP ? n : lim_min + row / GQ) : 0;   // positions this row sees
   const int g_full = min(t_end, lim_min) / 16;        // steps every row sees whole
   const int g_last = (t_end + 15) / 16;
@@ -1560,11 +1574,13 @@ bool dispatch_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, h
 // sequence is one unit of length 0 (it writes zeros).  Workgroups start in
 // id order, so the device stays full until the shortest units, which start
 // last.  Returns the count, or -1 when they do not fit one list.
-int order_units(const int32_t* host_lens, int S, int max_ctx, int part, bool equal, UnitList<true>& ul) {
+int order_units(const int32_t* host_lens, int S, int max_ctx, int part, bool equal, UnitList<true>& ul,
+                bool keep_empty = true) {
   struct U { int len, s, step; };
   std::vector<U> units;
   for (int s = 0; s < S; ++s) {
     const int n = std::min(std::max(host_lens[s], 0), max_ctx);
+    if (n == 0 && !keep_empty) continue;
     const int np = n > 0 ? (n + part - 1) / part : 1;
     const int plen = (equal && np > 1) ? ((n + np - 1) / np + 15) / 16 * 16 : part;
     if ((int64_t)n > ((int64_t)1 << kUnitStepBits) * 16 - plen) return -1;
@@ -1635,7 +1651,8 @@ void launch_mq_rows(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
 
 template <bool BF16, int GQ, int BS>
 void launch_mq_mfma(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mq_mfma_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
+  hipLaunchKernelGGL((mq_mfma_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args,
+                     UnitList<false>{});
   if (args.nparts_max > 1)
     hipLaunchKernelGGL((decode_merge_kernel<BF16, 16, 16 / GQ>), dim3(args.Hkv, args.S, args.ntiles), dim3(16 * 16),
                        0, stream, args);
@@ -1810,13 +1827,13 @@ constexpr int suffix_waves(int G) { return G <= 4 ? 1 : 2; }
 constexpr int kSuffixPart = 16 * 16;   // 16 steps of 16 tokens per partition
 
 GroupedLayout grouped_layout(int S, int Hkv, int G, int max_suffix, int ngroups, int max_group, int max_shared,
-                             bool shortest) {
+                             bool shortest, bool ordered = false) {
   GroupedLayout w;
   w.gntiles = ngroups > 0 ? (int)(((int64_t)max_group * G + 15) / 16) : 0;
   if (shortest) {   // the shortest partition the launcher can pick: a bound for every call
     w.gcfg.part_tokens = 16 * kWaves;
   } else {
-    w.gcfg = choose_launch(ngroups * w.gntiles, Hkv, max_shared);
+    w.gcfg = choose_launch(ngroups * w.gntiles, Hkv, max_shared, ordered);
     // a lane of a group-pass wave holds the block of one of its steps
     w.gcfg.part_tokens = std::min(w.gcfg.part_tokens, 16 * 64 * kGroupWaves);
   }
@@ -1835,9 +1852,13 @@ GroupedLayout grouped_layout(int S, int Hkv, int G, int max_suffix, int ngroups,
 
 template <bool BF16, int G, int BS>
 void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3 sgrid, const DecodeArgs& ma,
-                    hipStream_t stream) {
-  if (ggrid.x > 0)
-    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kGroupWaves, true>), ggrid, dim3(kGroupWaves * 64), 0, stream, ga);
+                    const UnitList<true>* gul, hipStream_t stream) {
+  if (gul != nullptr)
+    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kGroupWaves, true, true>),
+                       dim3((unsigned)(gul->count * ga.ntiles * ga.Hkv)), dim3(kGroupWaves * 64), 0, stream, ga, *gul);
+  else if (ggrid.x > 0)
+    hipLaunchKernelGGL((mq_mfma_kernel<BF16, G, BS, kGroupWaves, true>), ggrid, dim3(kGroupWaves * 64), 0, stream, ga,
+                       UnitList<false>{});
   constexpr int NWS = suffix_waves(G);
   static_assert(NWS * 64 >= G * 16, "the decode kernel needs G * 16 threads");
   hipLaunchKernelGGL((decode_attention_kernel<BF16, G, BS, NWS, 0, true>), sgrid, dim3(NWS * 64), 0, stream, sa,
@@ -1847,12 +1868,13 @@ void launch_grouped(const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3
 
 template <bool BF16, int BS>
 bool dispatch_grouped(int G, const DecodeArgs& ga, dim3 ggrid, const DecodeArgs& sa, dim3 sgrid, const DecodeArgs& ma,
+                      const UnitList<true>* gul,
                       hipStream_t stream) {
   switch (G) {
-    case 1: launch_grouped<BF16, 1, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
-    case 2: launch_grouped<BF16, 2, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
-    case 4: launch_grouped<BF16, 4, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
-    case 8: launch_grouped<BF16, 8, BS>(ga, ggrid, sa, sgrid, ma, stream); return true;
+    case 1: launch_grouped<BF16, 1, BS>(ga, ggrid, sa, sgrid, ma, gul, stream); return true;
+    case 2: launch_grouped<BF16, 2, BS>(ga, ggrid, sa, sgrid, ma, gul, stream); return true;
+    case 4: launch_grouped<BF16, 4, BS>(ga, ggrid, sa, sgrid, ma, gul, stream); return true;
+    case 8: launch_grouped<BF16, 8, BS>(ga, ggrid, sa, sgrid, ma, gul, stream); return true;
     default: return false;
   }
 }
@@ -1861,7 +1883,8 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
                          const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx,
                          const int32_t* group_start, const int32_t* group_len, const int32_t* seq_group, int ngroups,
                          int max_group, int max_shared, int max_suffix, float scale, void* workspace, size_t ws_bytes,
-                         const void* k_new, const void* v_new, const int64_t* slot_mapping, hipStream_t stream) {
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping, hipStream_t stream,
+                         const int32_t* host_group_len = nullptr) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
   if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
@@ -1891,7 +1914,8 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
       return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
   }
-  const GroupedLayout wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false);
+  const bool ordered = host_group_len != nullptr && ngroups > 0;
+  const GroupedLayout wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false, ordered);
   char* ws = static_cast<char*>(workspace);
   if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
   if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_grouped_workspace_bytes");
@@ -1954,19 +1978,32 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
   const uint64_t swg = (uint64_t)pool->Hkv * S * wl.scfg.nparts_max;
   if (gwg > 0x7fffffffULL || swg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   const dim3 ggrid((unsigned)gwg), sgrid((unsigned)swg);
+  // group pass in longest-first order over equal partitions of each
+  // group's shared positions (as the kernels count them: capped at
+  // max_shared and rounded down to 16)
+  static thread_local UnitList<true> gunits;
+  const UnitList<true>* gul = nullptr;
+  if (ordered && gwg > 0) {
+    std::vector<int32_t> shared(ngroups);
+    for (int g = 0; g < ngroups; ++g) shared[g] = std::min(std::max(host_group_len[g], 0), max_shared) & ~15;
+    ga.equal_chunks = 1;
+    if (order_units(shared.data(), ngroups, max_shared, wl.gcfg.part_tokens, true, gunits, false) > 0 &&
+        (int64_t)gunits.count * wl.gntiles * pool->Hkv <= 0x7fffffffLL)
+      gul = &gunits;
+  }
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
   switch (pool->B) {
-    case 8: ok = bf16 ? dispatch_grouped<true, 8>(G, ga, ggrid, sa, sgrid, args, stream)
-                      : dispatch_grouped<false, 8>(G, ga, ggrid, sa, sgrid, args, stream); break;
-    case 16: ok = bf16 ? dispatch_grouped<true, 16>(G, ga, ggrid, sa, sgrid, args, stream)
-                       : dispatch_grouped<false, 16>(G, ga, ggrid, sa, sgrid, args, stream); break;
-    case 32: ok = bf16 ? dispatch_grouped<true, 32>(G, ga, ggrid, sa, sgrid, args, stream)
-                       : dispatch_grouped<false, 32>(G, ga, ggrid, sa, sgrid, args, stream); break;
-    case 64: ok = bf16 ? dispatch_grouped<true, 64>(G, ga, ggrid, sa, sgrid, args, stream)
-                       : dispatch_grouped<false, 64>(G, ga, ggrid, sa, sgrid, args, stream); break;
-    default: ok = bf16 ? dispatch_grouped<true, 128>(G, ga, ggrid, sa, sgrid, args, stream)
-                       : dispatch_grouped<false, 128>(G, ga, ggrid, sa, sgrid, args, stream); break;
+    case 8: ok = bf16 ? dispatch_grouped<true, 8>(G, ga, ggrid, sa, sgrid, args, gul, stream)
+                      : dispatch_grouped<false, 8>(G, ga, ggrid, sa, sgrid, args, gul, stream); break;
+    case 16: ok = bf16 ? dispatch_grouped<true, 16>(G, ga, ggrid, sa, sgrid, args, gul, stream)
+                       : dispatch_grouped<false, 16>(G, ga, ggrid, sa, sgrid, args, gul, stream); break;
+    case 32: ok = bf16 ? dispatch_grouped<true, 32>(G, ga, ggrid, sa, sgrid, args, gul, stream)
+                       : dispatch_grouped<false, 32>(G, ga, ggrid, sa, sgrid, args, gul, stream); break;
+    case 64: ok = bf16 ? dispatch_grouped<true, 64>(G, ga, ggrid, sa, sgrid, args, gul, stream)
+                       : dispatch_grouped<false, 64>(G, ga, ggrid, sa, sgrid, args, gul, stream); break;
+    default: ok = bf16 ? dispatch_grouped<true, 128>(G, ga, ggrid, sa, sgrid, args, gul, stream)
+                       : dispatch_grouped<false, 128>(G, ga, ggrid, sa, sgrid, args, gul, stream); break;
   }
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
   return hip_check(hipGetLastError(), "grouped decode attention launch");
@@ -2066,6 +2103,20 @@ pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, 
   }
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
                        ws_bytes, k, v, slot_mapping, nullptr, 0, 0, stream);
+}
+
+pa_status pa_decode_attention_grouped_ordered(pa_pool* pool, int layer, const void* k, const void* v,
+                                              const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+                                              const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                              int max_ctx, const int32_t* group_start, const int32_t* group_len,
+                                              const int32_t* seq_group, const int32_t* host_group_len, int n_groups,
+                                              int max_group, int max_shared, int max_suffix, float scale,
+                                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (n_groups > 0 && !host_group_len) return fail(PA_ERR_INVALID_ARG, "NULL host_group_len");
+  return grouped_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, group_start, group_len,
+                        seq_group, n_groups, max_group, max_shared, max_suffix, scale, workspace, ws_bytes, k, v,
+                        slot_mapping, stream, host_group_len);
 }
 
 size_t pa_decode_grouped_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx, int n_groups,

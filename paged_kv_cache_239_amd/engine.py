@@ -81,6 +81,7 @@ class DecodeEngine:
         self.d_group_len = torch.zeros(S, dtype=torch.int32, device=device)
         self.d_seq_group = torch.zeros(S, dtype=torch.int32, device=device)
         self.n_groups = self.max_group = self.max_shared = self.max_suffix = 0
+        self.host_group_len = np.zeros(0, dtype=np.int32)
         self.gws = None
         self.gws_bytes = 0
         self._gcap = 0
@@ -139,6 +140,7 @@ class DecodeEngine:
         if self.grouped:
             gs, gl, sg, self.max_group, self.max_shared = self.pool.prefix_groups(self.tables, self.lens)
             self.n_groups = len(gl)
+            self.host_group_len = np.asarray(gl, dtype=np.int32).copy()
             self.max_suffix = int(np.max(self.lens - gl[sg])) if S else 0
         j, buf = self._staging.next()
         o = 0
@@ -225,7 +227,8 @@ class DecodeEngine:
                     self.d_group_start[: self.n_groups + 1], self.d_group_len[: self.n_groups], self.d_seq_group,
                     self.max_group, self.max_shared, self.max_suffix, scale, self.gws,
                     k=knews[layer] if fused else None, v=vnews[layer] if fused else None,
-                    slot_mapping=self.d_slots if fused else None, stream=stream)
+                    slot_mapping=self.d_slots if fused else None, stream=stream,
+                    host_group_len=self.host_group_len if self.ordered else None)
             elif self.ordered:
                 fused = self.fused
                 self.pool.decode_attention_ordered(

@@ -301,18 +301,31 @@ class Pool:
 
     def decode_attention_grouped(self, layer: int, out, q, block_tables, context_lens, max_ctx: int, group_start,
                                  group_len, seq_group, max_group: int, max_shared: int, max_suffix: int,
-                                 scale: float, workspace, k=None, v=None, slot_mapping=None, stream=None) -> None:
+                                 scale: float, workspace, k=None, v=None, slot_mapping=None, stream=None,
+                                 host_group_len=None) -> None:
         """Decode attention reading each group's shared prefix once (see
         pa_decode_attention_grouped); with k, v, slot_mapping the step's
         cache write is done in the same pass.  group_start: device int32
         [n_groups+1]; group_len: device int32 [n_groups]; seq_group: device
-        int32 [S]."""
+        int32 [S].  With ``host_group_len`` (host int32 [n_groups], equal to
+        group_len) the group pass runs longest first
+        (pa_decode_attention_grouped_ordered)."""
         S, Hq = int(q.shape[0]), int(q.shape[1])
         maxb = int(block_tables.shape[1])
         ng = int(group_start.shape[0]) - 1
         kp = _ptr(k) if k is not None else None
         vp = _ptr(v) if v is not None else None
         sp = _ptr(slot_mapping) if slot_mapping is not None else None
+        if host_group_len is not None:
+            hg = np.ascontiguousarray(host_group_len, dtype=np.int32)
+            if hg.shape != (ng,):
+                raise ValueError("host_group_len must hold one length per group")
+            check(self.lib, self.lib.pa_decode_attention_grouped_ordered(
+                self.handle, layer, C.c_void_p(kp), C.c_void_p(vp), C.c_void_p(sp), _ptr(out), _ptr(q), S, Hq,
+                _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), _ptr(group_start), _ptr(group_len),
+                _ptr(seq_group), hg.ctypes.data, ng, int(max_group), int(max_shared), int(max_suffix),
+                C.c_float(scale), _ptr(workspace), C.c_size_t(int(workspace.numel())), _stream_handle(stream)))
+            return
         check(self.lib, self.lib.pa_decode_attention_grouped(
             self.handle, layer, C.c_void_p(kp), C.c_void_p(vp), C.c_void_p(sp), _ptr(out), _ptr(q), S, Hq,
             _ptr(block_tables), maxb, _ptr(context_lens), int(max_ctx), _ptr(group_start), _ptr(group_len),

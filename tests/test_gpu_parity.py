@@ -876,14 +876,16 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
     ws = torch.empty(pool.grouped_workspace_bytes(S, Hq, max_ctx, len(gl), mg, ms, max_suffix), dtype=torch.uint8,
                      device="cuda")
     dq = to_device_bits(q, dtype)
-    out = torch.full_like(dq, float("nan"))
-    pool.decode_attention_grouped(0, out, dq, torch.from_numpy(tab).cuda(),
-                                  torch.tensor(lens, dtype=torch.int32, device="cuda"), max_ctx,
-                                  torch.from_numpy(gs).cuda(), torch.from_numpy(gl).cuda(), torch.from_numpy(sg).cuda(),
-                                  mg, ms, max_suffix, scale, ws)
-    torch.cuda.synchronize()
-    got = to_host_f64(out, dtype)
     ref = decode_layer(host, 0, q, tab, lens, scale, dtype)
-    ok, st = within_tolerance(got, ref)
-    _say(f"stats {st}")
-    assert ok, st
+    # the fixed grid, then the group pass longest first over equal partitions
+    for hgl in (None, gl):
+        out = torch.full_like(dq, float("nan"))
+        pool.decode_attention_grouped(0, out, dq, torch.from_numpy(tab).cuda(),
+                                      torch.tensor(lens, dtype=torch.int32, device="cuda"), max_ctx,
+                                      torch.from_numpy(gs).cuda(), torch.from_numpy(gl).cuda(),
+                                      torch.from_numpy(sg).cuda(), mg, ms, max_suffix, scale, ws, host_group_len=hgl)
+        torch.cuda.synchronize()
+        got = to_host_f64(out, dtype)
+        ok, st = within_tolerance(got, ref)
+        _say(f"ordered={hgl is not None} stats {st}")
+        assert ok, st
