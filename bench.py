@@ -500,7 +500,8 @@ def multi_query_bench(args) -> int:
             if events is not None and layer == events[2]:
                 events[0].record()
             eng.pool.multi_query_attention(layer, outs[layer], qs[layer], q_start, eng.d_tables, eng.d_lens,
-                                           max_ctx, Q, scale, workspace=ws)
+                                           max_ctx, Q, scale, workspace=ws,
+                                           host_context_lens=eng.lens if args.order == "on" else None)
             if events is not None and layer == events[2]:
                 events[1].record()
         return eng.lens.copy()

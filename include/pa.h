@@ -408,6 +408,27 @@ pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out,
                                    void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 
+/* pa_multi_query_attention with the context partitions launched longest
+ * first, as pa_decode_attention_ordered does, when each sequence's query
+ * rows (query tokens x query heads of a key/value head) fit one 16-row
+ * matrix-core tile, e.g. 4 speculative tokens at Hq / Hkv = 4.  Other
+ * shapes run as pa_multi_query_attention does.
+ *   host_context_lens : host int32 [S], equal to what context_lens holds
+ *                       when the launch executes; read during the call.
+ * Other arguments, results, errors and workspace as for
+ * pa_multi_query_attention; INVALID_ARG if host_context_lens is NULL while
+ * S > 0.  Outputs agree with pa_multi_query_attention within rounding (the
+ * partitions differ), and are deterministic. */
+pa_status pa_multi_query_attention_ordered(pa_pool* pool, int layer, void* out,
+                                           const void* q, const int32_t* q_start,
+                                           int T, int S, int Hq,
+                                           const int32_t* block_tables, int maxb,
+                                           const int32_t* context_lens,
+                                           const int32_t* host_context_lens,
+                                           int max_ctx, int max_q, float scale,
+                                           void* workspace, size_t ws_bytes,
+                                           hipStream_t stream);
+
 /* Decode attention (optionally with the step's cache write, as
  * pa_write_kv_decode_attention) for a batch in which groups of consecutive
  * sequences share a prefix: the parallel samples or beams of one prompt map

@@ -974,7 +974,8 @@ constexpr int kKRow = 272;   // bytes per token row of an LDS key tile (256 + 16
 // result is always left as partials for the cascade merge.
 template <bool BF16, int GQ, int BS, int NW, bool GRP = false, bool SCHED = false>
 __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, const UnitList<SCHED> ul) {
-  static_assert(!SCHED || GRP, "unit lists order the group pass");
+  // unit lists order the group pass, and several queries per sequence when
+  // a sequence's rows fit one tile (its tile context is then its length)
   constexpr int R = 16;             // rows per workgroup
   constexpr int QT = R / GQ;        // query tokens per workgroup
   static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
@@ -1650,6 +1651,26 @@ void launch_mq_rows(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
 }
 
 template <bool BF16, int GQ, int BS>
+void launch_mq_mfma_ordered(const DecodeArgs& args, const UnitList<true>& ul, hipStream_t stream) {
+  hipLaunchKernelGGL((mq_mfma_kernel<BF16, GQ, BS, kWaves, false, true>),
+                     dim3((unsigned)(ul.count * args.ntiles * args.Hkv)), dim3(kWaves * 64), 0, stream, args, ul);
+  if (args.nparts_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, 16, 16 / GQ>), dim3(args.Hkv, args.S, args.ntiles), dim3(16 * 16),
+                       0, stream, args);
+}
+
+template <bool BF16, int BS>
+bool dispatch_mq_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_mq_mfma_ordered<BF16, 1, BS>(args, ul, stream); return true;
+    case 2: launch_mq_mfma_ordered<BF16, 2, BS>(args, ul, stream); return true;
+    case 4: launch_mq_mfma_ordered<BF16, 4, BS>(args, ul, stream); return true;
+    case 8: launch_mq_mfma_ordered<BF16, 8, BS>(args, ul, stream); return true;
+    default: return false;
+  }
+}
+
+template <bool BF16, int GQ, int BS>
 void launch_mq_mfma(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((mq_mfma_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args,
                      UnitList<false>{});
@@ -1719,7 +1740,8 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const int ntiles = plan.ntiles;
   const int rows = multi ? plan.rows : G;
 
-  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, !multi && host_lens != nullptr);
+  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx,
+                                host_lens != nullptr && (!multi || (plan.mfma && !plan.wide && ntiles == 1)));
   if (multi && plan.wide && cfg.part_tokens > kWidePartMax) {
     cfg.part_tokens = kWidePartMax;
     cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
@@ -1766,6 +1788,24 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
+  // several queries per sequence: ordered on the 16-row matrix path when a
+  // sequence's rows fit one tile
+  const bool mq_ordered = multi && host_lens != nullptr && plan.mfma && !plan.wide && ntiles == 1;
+  if (mq_ordered) {
+    static thread_local UnitList<true> mul;
+    args.equal_chunks = 1;
+    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, true, mul) > 0) {
+      switch (pool->B) {
+        case 8: ok = bf16 ? dispatch_mq_ordered<true, 8>(G, args, mul, stream) : dispatch_mq_ordered<false, 8>(G, args, mul, stream); break;
+        case 16: ok = bf16 ? dispatch_mq_ordered<true, 16>(G, args, mul, stream) : dispatch_mq_ordered<false, 16>(G, args, mul, stream); break;
+        case 32: ok = bf16 ? dispatch_mq_ordered<true, 32>(G, args, mul, stream) : dispatch_mq_ordered<false, 32>(G, args, mul, stream); break;
+        case 64: ok = bf16 ? dispatch_mq_ordered<true, 64>(G, args, mul, stream) : dispatch_mq_ordered<false, 64>(G, args, mul, stream); break;
+        default: ok = bf16 ? dispatch_mq_ordered<true, 128>(G, args, mul, stream) : dispatch_mq_ordered<false, 128>(G, args, mul, stream); break;
+      }
+      if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+      return hip_check(hipGetLastError(), "multi-query attention launch");
+    }
+  }
   if (!multi && host_lens != nullptr) {
     static thread_local UnitList<true> ul;
     args.equal_chunks = 1;
@@ -2088,6 +2128,18 @@ pa_status pa_multi_query_attention(pa_pool* pool, int layer, void* out, const vo
   if (S > 0 && !q_start) return fail(PA_ERR_INVALID_ARG, "NULL q_start");
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
                        ws_bytes, nullptr, nullptr, nullptr, q_start, T, max_q, stream);
+}
+
+pa_status pa_multi_query_attention_ordered(pa_pool* pool, int layer, void* out, const void* q,
+                                           const int32_t* q_start, int T, int S, int Hq,
+                                           const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                           const int32_t* host_context_lens, int max_ctx, int max_q, float scale,
+                                           void* workspace, size_t ws_bytes, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (S > 0 && !q_start) return fail(PA_ERR_INVALID_ARG, "NULL q_start");
+  if (S > 0 && !host_context_lens) return fail(PA_ERR_INVALID_ARG, "NULL host_context_lens");
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
+                       ws_bytes, nullptr, nullptr, nullptr, q_start, T, max_q, stream, host_context_lens);
 }
 
 pa_status pa_write_kv_decode_attention(pa_pool* pool, int layer, const void* k, const void* v,

@@ -281,14 +281,27 @@ class Pool:
             _stream_handle(stream)))
 
     def multi_query_attention(self, layer: int, out, q, q_start, block_tables, context_lens, max_ctx: int,
-                              max_q: int, scale: float, workspace=None, stream=None) -> None:
+                              max_q: int, scale: float, workspace=None, stream=None,
+                              host_context_lens=None) -> None:
         """out, q: device [T][Hq][d]; q_start: device int32 [S+1] (queries of
         sequence s are rows q_start[s] .. q_start[s+1]-1, its last positions);
-        block_tables: device int32 [S][maxb]; context_lens: device int32 [S]."""
+        block_tables: device int32 [S][maxb]; context_lens: device int32 [S].
+        With ``host_context_lens`` (host int32 [S], equal to context_lens)
+        the partitions run longest first where the shape allows
+        (pa_multi_query_attention_ordered)."""
         T, Hq = int(q.shape[0]), int(q.shape[1])
         S = int(q_start.shape[0]) - 1
         maxb = int(block_tables.shape[1])
         ws_ptr, ws_bytes = (0, 0) if workspace is None else (_ptr(workspace), int(workspace.numel()))
+        if host_context_lens is not None:
+            hl = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+            if hl.shape != (S,):
+                raise ValueError("host_context_lens must hold one length per sequence")
+            check(self.lib, self.lib.pa_multi_query_attention_ordered(
+                self.handle, layer, _ptr(out), _ptr(q), _ptr(q_start), T, S, Hq, _ptr(block_tables), maxb,
+                _ptr(context_lens), hl.ctypes.data, int(max_ctx), int(max_q), C.c_float(scale),
+                C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
+            return
         check(self.lib, self.lib.pa_multi_query_attention(
             self.handle, layer, _ptr(out), _ptr(q), _ptr(q_start), T, S, Hq, _ptr(block_tables), maxb,
             _ptr(context_lens), int(max_ctx), int(max_q), C.c_float(scale), C.c_void_p(ws_ptr or None),

@@ -707,7 +707,7 @@ MQ_SHAPES = [
 ]
 
 
-def _mq_case(rng, G, Hkv, B, dtype, lens, nqs):
+def _mq_case(rng, G, Hkv, B, dtype, lens, nqs, ordered=False):
     from oracle.decode import multi_query_one
     from paged_kv_cache_239_amd import multi_query_workspace
     S = len(lens)
@@ -723,7 +723,7 @@ def _mq_case(rng, G, Hkv, B, dtype, lens, nqs):
     out = torch.full_like(dq, float("nan"))
     pool.multi_query_attention(0, out, dq, torch.from_numpy(q_start).cuda(), torch.from_numpy(tables).cuda(),
                                torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(), max(lens), max_q, scale,
-                               workspace=ws)
+                               workspace=ws, host_context_lens=np.asarray(lens, dtype=np.int32) if ordered else None)
     torch.cuda.synchronize()
     got = to_host_f64(out, dtype)
     worst = 0.0
@@ -784,6 +784,19 @@ def test_multi_query_matrix_path_16_rows(G, Hkv, B, dtype, max_q):
     lens = [max_q, 40, 129, 1000, 2500]
     nqs = [max_q, 3, max_q, 1, max_q - 1]
     _mq_case(rng, G, Hkv, B, dtype, lens, nqs)
+
+
+@pytest.mark.parametrize("G,Hkv,B,dtype,max_q", [(4, 2, 16, "bf16", 4), (1, 4, 32, "f16", 12), (2, 2, 8, "bf16", 6),
+                                                 (8, 1, 64, "f16", 2)])
+def test_multi_query_ordered_one_tile(G, Hkv, B, dtype, max_q):
+    """9 to 16 rows per sequence (one matrix-core tile), partitions of equal
+    length launched longest first from host copies of the lengths, against
+    the oracle; also the same inputs in the fixed grid order."""
+    _say(f"multi-query ordered G={G} max_q={max_q}")
+    lens = [max_q, 40, 129, 1000, 2500, 1536, 4097, 700]
+    nqs = [max_q, 1, max_q, 2, max_q - 1, max_q, max_q, 1]
+    for ordered in (False, True):
+        _mq_case(np.random.default_rng(900 + G), G, Hkv, B, dtype, lens, nqs, ordered=ordered)
 
 
 # --------------------------------------------------------------------------------
