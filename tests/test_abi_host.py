@@ -248,3 +248,26 @@ def test_workload_histories_bit_exact(cfg):
     for s in range(wl.S):
         nb = -(-int(lens[s]) // wl.cfg.B)
         assert list(tables[s, :nb]) == st.tables[s][:nb]
+
+
+def test_ordered_entry_points_check_host_arguments_first():
+    """The ordered calls reject a missing host copy of the lengths, and a
+    fused call given only some of k, v, slot_mapping, before any device
+    work (so this runs without a GPU)."""
+    import ctypes as C
+    lib = _abi.load()
+    fake = C.c_void_p(256)   # never dereferenced: the checks come first
+    hl = np.array([10, 20], dtype=np.int32)
+    st = lib.pa_decode_attention_ordered(None, 0, None, None, None, fake, fake, 2, 8, fake, 4, fake, None, 20,
+                                         C.c_float(0.1), None, 0, None)
+    assert st == _abi.PA_ERR_INVALID_ARG and b"host_context_lens" in lib.pa_last_error()
+    st = lib.pa_decode_attention_ordered(None, 0, fake, None, None, fake, fake, 2, 8, fake, 4, fake,
+                                         hl.ctypes.data, 20, C.c_float(0.1), None, 0, None)
+    assert st == _abi.PA_ERR_INVALID_ARG and b"slot_mapping" in lib.pa_last_error()
+    st = lib.pa_multi_query_attention_ordered(None, 0, fake, fake, fake, 4, 2, 8, fake, 4, fake, None, 20, 2,
+                                              C.c_float(0.1), None, 0, None)
+    assert st == _abi.PA_ERR_INVALID_ARG and b"host_context_lens" in lib.pa_last_error()
+    st = lib.pa_decode_attention_grouped_ordered(None, 0, None, None, None, fake, fake, 2, 8, fake, 4, fake, 20,
+                                                 fake, fake, fake, None, 1, 2, 16, 4, C.c_float(0.1), fake, 1 << 20,
+                                                 None)
+    assert st == _abi.PA_ERR_INVALID_ARG and b"host_group_len" in lib.pa_last_error()
