@@ -283,7 +283,6 @@ struct DecodeArgs {
   const int64_t* slots;     // [S] their slots, or null
   int64_t nslots;           // P * B
   int S, Hq, Hkv, P, maxb, max_ctx, part_tokens, nparts_max;
-  int equal_chunks = 0;     // unit lists: a sequence's partitions share its length equally
   int grid_order;           // see decode_attention_kernel
   int pstride;              // partitions per (sequence, head) in grid order 1
   float scale_log2;         // softmax scale * log2(e)
@@ -436,11 +435,11 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   n = __builtin_amdgcn_readfirstlane(n);
   const int nparts = SUF ? (n - start + a.part_tokens - 1) / a.part_tokens
                          : (n > 0 ? (n + a.part_tokens - 1) / a.part_tokens : 1);
-  // Partition length: part_tokens, or with equal chunks the sequence's
+  // Partition length: part_tokens, or from a unit list, the sequence's
   // nparts partitions share its length (rounded up to 16 tokens).
   int plen = a.part_tokens;
   if constexpr (SCHED) {
-    if (a.equal_chunks && nparts > 1) plen = ((n + nparts - 1) / nparts + 15) & ~15;
+    if (nparts > 1) plen = ((n + nparts - 1) / nparts + 15) & ~15;
     if (t_begin % plen) return;   // not a partition start of this length
     p = t_begin / plen;
   }
@@ -1568,14 +1567,14 @@ bool dispatch_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, h
   }
 }
 
-// The units of a decode launch, longest first.  With `equal` a sequence
-// of n positions gets np = ceil(n / part) partitions of equal length
-// (ceil(n / np) rounded up to 16; the last may be shorter by the rounding),
-// otherwise full partitions of `part` and a shorter last one.  An empty
-// sequence is one unit of length 0 (it writes zeros).  Workgroups start in
-// id order, so the device stays full until the shortest units, which start
-// last.  Returns the count, or -1 when they do not fit one list.
-int order_units(const int32_t* host_lens, int S, int max_ctx, int part, bool equal, UnitList<true>& ul,
+// The units of a decode launch, longest first.  A sequence of n positions
+// gets np = ceil(n / part) partitions of equal length (ceil(n / np) rounded
+// up to 16; the last may be shorter by the rounding), so no partition is a
+// short remainder.  An empty sequence is one unit of length 0 (it writes
+// zeros) unless `keep_empty` is false.  Workgroups start in id order, so the
+// device stays full until the shortest units, which start last.  Returns
+// the count, or -1 when they do not fit one list.
+int order_units(const int32_t* host_lens, int S, int max_ctx, int part, UnitList<true>& ul,
                 bool keep_empty = true) {
   struct U { int len, s, step; };
   std::vector<U> units;
@@ -1583,7 +1582,7 @@ int order_units(const int32_t* host_lens, int S, int max_ctx, int part, bool equ
     const int n = std::min(std::max(host_lens[s], 0), max_ctx);
     if (n == 0 && !keep_empty) continue;
     const int np = n > 0 ? (n + part - 1) / part : 1;
-    const int plen = (equal && np > 1) ? ((n + np - 1) / np + 15) / 16 * 16 : part;
+    const int plen = np > 1 ? ((n + np - 1) / np + 15) / 16 * 16 : part;
     if ((int64_t)n > ((int64_t)1 << kUnitStepBits) * 16 - plen) return -1;
     for (int p = 0; p < np; ++p) {
       units.push_back({std::max(std::min(plen, n - p * plen), 0), s, p * plen / 16});
@@ -1793,8 +1792,7 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const bool mq_ordered = multi && host_lens != nullptr && plan.mfma && !plan.wide && ntiles == 1;
   if (mq_ordered) {
     static thread_local UnitList<true> mul;
-    args.equal_chunks = 1;
-    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, true, mul) > 0) {
+    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, mul) > 0) {
       switch (pool->B) {
         case 8: ok = bf16 ? dispatch_mq_ordered<true, 8>(G, args, mul, stream) : dispatch_mq_ordered<false, 8>(G, args, mul, stream); break;
         case 16: ok = bf16 ? dispatch_mq_ordered<true, 16>(G, args, mul, stream) : dispatch_mq_ordered<false, 16>(G, args, mul, stream); break;
@@ -1808,8 +1806,7 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   }
   if (!multi && host_lens != nullptr) {
     static thread_local UnitList<true> ul;
-    args.equal_chunks = 1;
-    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, true, ul) > 0) {
+    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0) {
       switch (pool->B) {
         case 8: ok = bf16 ? dispatch_ordered<true, 8>(G, args, ul, stream) : dispatch_ordered<false, 8>(G, args, ul, stream); break;
         case 16: ok = bf16 ? dispatch_ordered<true, 16>(G, args, ul, stream) : dispatch_ordered<false, 16>(G, args, ul, stream); break;
@@ -2026,8 +2023,7 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
   if (ordered && gwg > 0) {
     std::vector<int32_t> shared(ngroups);
     for (int g = 0; g < ngroups; ++g) shared[g] = std::min(std::max(host_group_len[g], 0), max_shared) & ~15;
-    ga.equal_chunks = 1;
-    if (order_units(shared.data(), ngroups, max_shared, wl.gcfg.part_tokens, true, gunits, false) > 0 &&
+    if (order_units(shared.data(), ngroups, max_shared, wl.gcfg.part_tokens, gunits, false) > 0 &&
         (int64_t)gunits.count * wl.gntiles * pool->Hkv <= 0x7fffffffLL)
       gul = &gunits;
   }
