@@ -170,9 +170,10 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
-                                   "part of this build (each GPU would hold its own shard of heads "
-                                   "or sequences with no exchange inside attention)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the library has no "
+                                   "multi-GPU path (each GPU would hold its own shard of heads "
+                                   "or sequences with no exchange inside attention; --head-shards N "
+                                   "runs one GPU's share)",
                           "n_gpus": args.gpus}))
         return 2
 
