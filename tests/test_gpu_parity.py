@@ -352,17 +352,19 @@ def test_decode_partition_merge_with_garbage_and_reused_workspace():
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("case", ["ragged", "many"])
-def test_decode_ordered_matches_oracle_and_fixed_order(fused, case):
+@pytest.mark.parametrize("case,G,B,dtype", [("ragged", 4, 16, "bf16"), ("many", 4, 16, "bf16"),
+                                            ("ragged", 1, 8, "f16"), ("ragged", 2, 32, "bf16"),
+                                            ("ragged", 8, 128, "f16")])
+def test_decode_ordered_matches_oracle_and_fixed_order(fused, case, G, B, dtype):
     """Partitions of equal length launched longest first from host copies
     of the lengths: the oracle's outputs within tolerance, the same bits on
     a rerun, and (fused) the same pool as the fixed grid order; empty
     sequences, lengths at and around partition multiples.  "many" has more
     (sequence, partition) units than one list holds and runs as the fixed
     order does, bit for bit."""
-    _say(f"ordered launch {case} fused={fused}")
-    rng = np.random.default_rng(11)
-    dtype, B, Hkv, G = "bf16", 16, 2, 4
+    _say(f"ordered launch {case} G={G} B={B} {dtype} fused={fused}")
+    rng = np.random.default_rng(11 + G + B)
+    Hkv = 2
     if case == "ragged":
         lens = [0, 1, 383, 384, 385, 767, 768, 769, 1536, 2047, 4096, 5000, 12345, 3, 0, 900]
     else:
