@@ -1500,15 +1500,21 @@ struct LaunchCfg {
 // wave (1,536 tokens).  A workgroup is latency-bound: its first loads wait
 // for two memory round trips, so a short partition moves its bytes at a
 // fraction of a full one's rate; equal partitions have no short remainders
-// (config-3 batch: 98 us per layer, against 100-101 with full partitions
-// plus a remainder at 16-24 steps per wave, and 103-105 at 6-8).
+// (config-3 batch: 98 us per layer at 24 steps per wave, 101 at 12, against
+// 100-101 with full partitions plus a remainder at 16-24 steps per wave,
+// and 103-105 at 6-8).
 LaunchCfg choose_launch(int S, int Hkv, int max_ctx, bool ordered = false) {
   static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
   int gpw = ordered ? 24 : 12;
   if (forced > 0) {
     gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
   } else {
-    const int64_t target = 2048;  // workgroups: 256 CUs x 8
+    // workgroups: 256 CUs x 8 for the fixed grid, whose workgroups past a
+    // sequence's end cost little; a unit list holds live units only, and its
+    // partitions are worth keeping long down to about one per CU (one GPU's
+    // share of the GQA batch, 16/4 heads: 55.0 us per layer at 24 steps per
+    // wave, 58.0 at 6; 4/1 heads: 21.6 at 12, 23.7 at 6)
+    const int64_t target = ordered ? 256 : 2048;
     const int floor_gpw = max_ctx >= 2 * 16 * kWaves * 6 ? 6 : 1;
     while (gpw > floor_gpw) {
       const int64_t part = 16LL * kWaves * gpw;
