@@ -487,7 +487,9 @@ pa_status pa_decode_attention_grouped(pa_pool* pool, int layer, const void* k,
  * Other arguments, results, errors and workspace as for
  * pa_decode_attention_grouped; INVALID_ARG if host_group_len is NULL while
  * n_groups > 0.  Outputs agree with pa_decode_attention_grouped within
- * rounding (the group partitions differ), and are deterministic. */
+ * rounding (the group partitions differ), and are deterministic.  If the
+ * groups' partitions do not fit one list (over 512 units), the call runs as
+ * pa_decode_attention_grouped does. */
 pa_status pa_decode_attention_grouped_ordered(
     pa_pool* pool, int layer, const void* k, const void* v,
     const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,

@@ -1745,8 +1745,15 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const int ntiles = plan.ntiles;
   const int rows = multi ? plan.rows : G;
 
-  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx,
-                                host_lens != nullptr && (!multi || (plan.mfma && !plan.wide && ntiles == 1)));
+  // A unit list (longest first) when host lengths are given and the shape
+  // allows one: single-query decode, or several queries whose rows fit one
+  // 16-row matrix tile.  If the units do not fit a list, the launch is the
+  // unordered one, with its own partition length.
+  const bool want_list = host_lens != nullptr && (!multi || (plan.mfma && !plan.wide && ntiles == 1));
+  static thread_local UnitList<true> ul;
+  LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, want_list);
+  const bool use_list = want_list && order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0;
+  if (want_list && !use_list) cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, false);
   if (multi && plan.wide && cfg.part_tokens > kWidePartMax) {
     cfg.part_tokens = kWidePartMax;
     cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
@@ -1793,36 +1800,27 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
-  // several queries per sequence: ordered on the 16-row matrix path when a
-  // sequence's rows fit one tile
-  const bool mq_ordered = multi && host_lens != nullptr && plan.mfma && !plan.wide && ntiles == 1;
-  if (mq_ordered) {
-    static thread_local UnitList<true> mul;
-    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, mul) > 0) {
-      switch (pool->B) {
-        case 8: ok = bf16 ? dispatch_mq_ordered<true, 8>(G, args, mul, stream) : dispatch_mq_ordered<false, 8>(G, args, mul, stream); break;
-        case 16: ok = bf16 ? dispatch_mq_ordered<true, 16>(G, args, mul, stream) : dispatch_mq_ordered<false, 16>(G, args, mul, stream); break;
-        case 32: ok = bf16 ? dispatch_mq_ordered<true, 32>(G, args, mul, stream) : dispatch_mq_ordered<false, 32>(G, args, mul, stream); break;
-        case 64: ok = bf16 ? dispatch_mq_ordered<true, 64>(G, args, mul, stream) : dispatch_mq_ordered<false, 64>(G, args, mul, stream); break;
-        default: ok = bf16 ? dispatch_mq_ordered<true, 128>(G, args, mul, stream) : dispatch_mq_ordered<false, 128>(G, args, mul, stream); break;
-      }
-      if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
-      return hip_check(hipGetLastError(), "multi-query attention launch");
+  if (use_list && multi) {       // several queries per sequence, one tile each
+    switch (pool->B) {
+      case 8: ok = bf16 ? dispatch_mq_ordered<true, 8>(G, args, ul, stream) : dispatch_mq_ordered<false, 8>(G, args, ul, stream); break;
+      case 16: ok = bf16 ? dispatch_mq_ordered<true, 16>(G, args, ul, stream) : dispatch_mq_ordered<false, 16>(G, args, ul, stream); break;
+      case 32: ok = bf16 ? dispatch_mq_ordered<true, 32>(G, args, ul, stream) : dispatch_mq_ordered<false, 32>(G, args, ul, stream); break;
+      case 64: ok = bf16 ? dispatch_mq_ordered<true, 64>(G, args, ul, stream) : dispatch_mq_ordered<false, 64>(G, args, ul, stream); break;
+      default: ok = bf16 ? dispatch_mq_ordered<true, 128>(G, args, ul, stream) : dispatch_mq_ordered<false, 128>(G, args, ul, stream); break;
     }
+    if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+    return hip_check(hipGetLastError(), "multi-query attention launch");
   }
-  if (!multi && host_lens != nullptr) {
-    static thread_local UnitList<true> ul;
-    if (order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0) {
-      switch (pool->B) {
-        case 8: ok = bf16 ? dispatch_ordered<true, 8>(G, args, ul, stream) : dispatch_ordered<false, 8>(G, args, ul, stream); break;
-        case 16: ok = bf16 ? dispatch_ordered<true, 16>(G, args, ul, stream) : dispatch_ordered<false, 16>(G, args, ul, stream); break;
-        case 32: ok = bf16 ? dispatch_ordered<true, 32>(G, args, ul, stream) : dispatch_ordered<false, 32>(G, args, ul, stream); break;
-        case 64: ok = bf16 ? dispatch_ordered<true, 64>(G, args, ul, stream) : dispatch_ordered<false, 64>(G, args, ul, stream); break;
-        default: ok = bf16 ? dispatch_ordered<true, 128>(G, args, ul, stream) : dispatch_ordered<false, 128>(G, args, ul, stream); break;
-      }
-      if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
-      return hip_check(hipGetLastError(), "decode attention launch");
+  if (use_list) {
+    switch (pool->B) {
+      case 8: ok = bf16 ? dispatch_ordered<true, 8>(G, args, ul, stream) : dispatch_ordered<false, 8>(G, args, ul, stream); break;
+      case 16: ok = bf16 ? dispatch_ordered<true, 16>(G, args, ul, stream) : dispatch_ordered<false, 16>(G, args, ul, stream); break;
+      case 32: ok = bf16 ? dispatch_ordered<true, 32>(G, args, ul, stream) : dispatch_ordered<false, 32>(G, args, ul, stream); break;
+      case 64: ok = bf16 ? dispatch_ordered<true, 64>(G, args, ul, stream) : dispatch_ordered<false, 64>(G, args, ul, stream); break;
+      default: ok = bf16 ? dispatch_ordered<true, 128>(G, args, ul, stream) : dispatch_ordered<false, 128>(G, args, ul, stream); break;
     }
+    if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+    return hip_check(hipGetLastError(), "decode attention launch");
   }
   if (multi && plan.mfma) {
     switch (pool->B) {
@@ -1957,8 +1955,20 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
       return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
   }
-  const bool ordered = host_group_len != nullptr && ngroups > 0;
-  const GroupedLayout wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false, ordered);
+  // group pass in longest-first order over equal partitions of each group's
+  // shared positions (as the kernels count them: capped at max_shared and
+  // rounded down to 16); if they do not fit one list, the unordered layout
+  static thread_local UnitList<true> gunits;
+  bool use_list = false;
+  GroupedLayout wl;
+  if (host_group_len != nullptr && ngroups > 0 && max_shared >= 16) {
+    wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false, true);
+    std::vector<int32_t> shared(ngroups);
+    for (int g = 0; g < ngroups; ++g) shared[g] = std::min(std::max(host_group_len[g], 0), max_shared) & ~15;
+    use_list = order_units(shared.data(), ngroups, max_shared, wl.gcfg.part_tokens, gunits, false) > 0 &&
+               (int64_t)gunits.count * wl.gntiles * pool->Hkv <= 0x7fffffffLL;
+  }
+  if (!use_list) wl = grouped_layout(S, pool->Hkv, G, max_suffix, ngroups, max_group, max_shared, false);
   char* ws = static_cast<char*>(workspace);
   if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
   if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_grouped_workspace_bytes");
@@ -2021,18 +2031,7 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
   const uint64_t swg = (uint64_t)pool->Hkv * S * wl.scfg.nparts_max;
   if (gwg > 0x7fffffffULL || swg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   const dim3 ggrid((unsigned)gwg), sgrid((unsigned)swg);
-  // group pass in longest-first order over equal partitions of each
-  // group's shared positions (as the kernels count them: capped at
-  // max_shared and rounded down to 16)
-  static thread_local UnitList<true> gunits;
-  const UnitList<true>* gul = nullptr;
-  if (ordered && gwg > 0) {
-    std::vector<int32_t> shared(ngroups);
-    for (int g = 0; g < ngroups; ++g) shared[g] = std::min(std::max(host_group_len[g], 0), max_shared) & ~15;
-    if (order_units(shared.data(), ngroups, max_shared, wl.gcfg.part_tokens, gunits, false) > 0 &&
-        (int64_t)gunits.count * wl.gntiles * pool->Hkv <= 0x7fffffffLL)
-      gul = &gunits;
-  }
+  const UnitList<true>* gul = use_list ? &gunits : nullptr;
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
   switch (pool->B) {
