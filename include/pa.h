@@ -96,7 +96,11 @@ typedef struct {
  * product overflows. */
 size_t pa_pool_bytes(int L, int Hkv, int d, int B, int P, pa_dtype dtype);
 
-/* Create a pool over caller-provided device memory.
+/* Create a pool over caller-provided device memory: the "block engine" of
+ * "vLLM PagedAttention and continuous batching", section "PagedAttention:
+ * fixed blocks, non-contiguous physical memory" (one contiguous allocation
+ * sliced into physical blocks of B token slots; separate key and value
+ * caches, section "The kernel page").
  *   dev_base  : device, 256-byte aligned, at least pa_pool_bytes(...) bytes.
  *               Layout, layer-major with separate key and value slabs:
  *                 K of layer l at dev_base + (2l)   * slab
@@ -114,7 +118,9 @@ pa_status pa_alloc_pool(pa_pool** out, int L, int Hkv, int d, int B, int P,
                         const int32_t* free_order);
 void pa_free_pool(pa_pool* pool); /* host metadata only; NULL is a no-op */
 
-/* Device addresses of layer `layer`'s key and value slabs. */
+/* Device addresses of layer `layer`'s key and value slabs (the layout
+ * above).  INVALID_ARG for a NULL pool or output, or a layer outside
+ * [0, L). */
 pa_status pa_pool_layer_ptrs(const pa_pool* pool, int layer, void** k_slab,
                              void** v_slab);
 
@@ -123,14 +129,26 @@ pa_status pa_pool_layer_ptrs(const pa_pool* pool, int layer, void** k_slab,
  * Block tables are host int32 arrays of `maxb` entries; entry j is the
  * physical block of logical block j (tokens jB..jB+B-1).  A sequence of n
  * tokens uses entries 0..ceil(n/B)-1; the rest are ignored.
+ * Source: "vLLM PagedAttention and continuous batching", sections
+ * "PagedAttention: fixed blocks, non-contiguous physical memory" (the block
+ * table with its fill count; a new block only when the last one is full)
+ * and "Sharing with reference counts and copy-on-write" (reference counts;
+ * the fork, append and free policies; release at count 0).  The free list
+ * is first in, first out -- the pages leave the order open; this one keeps
+ * a released address out of reuse for as long as possible.
  * ------------------------------------------------------------------- */
 
-/* Pop the head of the free list; the block gets refcount 1. */
+/* Pop the head of the free list; the block gets refcount 1 (a new physical
+ * block for a sequence, section "PagedAttention: fixed blocks").
+ * OUT_OF_BLOCKS when the list is empty (nothing changes). */
 pa_status pa_block_alloc(pa_pool* pool, int32_t* blk);
-/* One more reference to a live block (INVALID_ARG if free or out of range). */
+/* One more reference to a live block: the fork policy of section "Sharing
+ * with reference counts and copy-on-write" (INVALID_ARG if free or out of
+ * range). */
 pa_status pa_block_incref(pa_pool* pool, int32_t blk);
-/* Drop one reference; at 0 the block goes to the tail of the free list.
- * INVALID_ARG for a block that is already free (double free). */
+/* Drop one reference; at 0 the block goes to the tail of the free list (the
+ * free policy of the same section).  INVALID_ARG for a block that is
+ * already free (double free) or out of range. */
 pa_status pa_block_decref(pa_pool* pool, int32_t blk);
 /* Current refcount, or -1 if blk is out of range. */
 int32_t pa_block_refcount(const pa_pool* pool, int32_t blk);
@@ -141,7 +159,9 @@ pa_status pa_free_list(const pa_pool* pool, int32_t* out, int32_t cap,
 pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
 
 /* Append one token to a sequence holding n_before tokens (its new token
- * goes to position n_before):
+ * goes to position n_before) -- the append policy with copy-on-write of
+ * "vLLM PagedAttention and continuous batching", sections "PagedAttention:
+ * fixed blocks" and "Sharing with reference counts and copy-on-write":
  *   - n_before % B == 0: take a new block for logical block n_before / B;
  *   - else if the block holding position n_before has refcount > 1
  *     (copy-on-write): take a new block, report (*cow_src, *cow_dst) =
@@ -155,7 +175,9 @@ pa_status pa_append_slot(pa_pool* pool, int32_t* table, int32_t maxb,
                          int32_t n_before, int64_t* slot, int32_t* cow_src,
                          int32_t* cow_dst);
 
-/* `count` successive appends to one sequence (prefill).  slots: host
+/* `count` successive appends to one sequence (prefill: "vLLM PagedAttention
+ * and continuous batching", section "How it works", writes the prompt's
+ * keys and values; each append follows pa_append_slot).  slots: host
  * [count] or NULL; cow_pairs: host [count][2] or NULL; *n_pairs = copies
  * requested; *n_done = appends completed.  On failure the first *n_done
  * appends stay applied and the failing one changed nothing. */
@@ -164,7 +186,9 @@ pa_status pa_append_tokens(pa_pool* pool, int32_t* table, int32_t maxb,
                            int32_t* cow_pairs, int32_t* n_pairs,
                            int32_t* n_done);
 
-/* One decode step for S sequences, processed in batch order (the first
+/* One decode step for S sequences (section "How it works": decode adds one
+ * token per sequence per iteration; each append follows pa_append_slot),
+ * processed in batch order (the first
  * writer into a shared block copies; the one that finds refcount 1 writes
  * in place).  tables: host [S][maxb] (edited in place); n_before: host [S];
  * slots: host [S]; cow_pairs: host [S][2]; *n_pairs, *n_done as above. */
@@ -173,14 +197,17 @@ pa_status pa_append_batch(pa_pool* pool, int32_t* tables, int32_t maxb,
                           int32_t* cow_pairs, int32_t* n_pairs,
                           int32_t* n_done);
 
-/* Fork: child_table[0..nb-1] = parent_table[0..nb-1] and one more reference
+/* Fork (section "Sharing with reference counts and copy-on-write": parallel
+ * samples and beams map the parent's blocks with one more reference each):
+ * child_table[0..nb-1] = parent_table[0..nb-1] and one more reference
  * to each of those blocks, nb = ceil(n_tokens / B).  Nothing changes on
  * error. */
 pa_status pa_seq_fork(pa_pool* pool, const int32_t* parent_table,
                       int32_t n_tokens, int32_t* child_table, int32_t maxb);
 
-/* Free: one reference fewer for each of the sequence's ceil(n_tokens/B)
- * blocks.  INVALID_ARG (and nothing changes) if a block would drop below
+/* Free (same section: a finished or dropped sequence releases its
+ * references; blocks at count 0 return to the free list): one reference
+ * fewer for each of the sequence's ceil(n_tokens/B) blocks.  INVALID_ARG (and nothing changes) if a block would drop below
  * zero. */
 pa_status pa_seq_free(pa_pool* pool, const int32_t* table, int32_t n_tokens);
 
@@ -240,13 +267,18 @@ pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables,
  * [S+1] (run g is sequences group_start[g] .. group_start[g+1]-1,
  * group_start[n_groups] = S), group_len [S] (shared length of each run),
  * seq_group [S] (the run of each sequence); *n_groups = runs, *max_group =
- * the largest run that shares, *max_shared = the largest shared length.
- * No state changes. */
+ * the largest run that shares, *max_shared = the largest shared length,
+ * *max_suffix = the largest number of positions a sequence holds outside
+ * its run's shared prefix (lens[s] - group_len[seq_group[s]]; the
+ * max_suffix argument of pa_decode_attention_grouped).
+ * No state changes.  INVALID_ARG for a NULL output or a length that does not
+ * fit the table. */
 pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables,
                            const int32_t* lens, int32_t S, int32_t maxb,
                            int32_t* group_start, int32_t* group_len,
                            int32_t* seq_group, int32_t* n_groups,
-                           int32_t* max_group, int32_t* max_shared);
+                           int32_t* max_group, int32_t* max_shared,
+                           int32_t* max_suffix);
 
 /* ---------------------------------------------------------------------
  * Device operations ("fused block operations" of the reading guide
@@ -254,7 +286,10 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables,
  * PagedAttention", section "Main concepts to understand")
  * ------------------------------------------------------------------- */
 
-/* reshape_and_cache: token s's key and value, k[s] and v[s] (device,
+/* reshape_and_cache ("vLLM PagedAttention and continuous batching", section
+ * "How it works": each step writes its token's key and value into the
+ * cache; the reading guide's "fused block operations"): token s's key and
+ * value, k[s] and v[s] (device,
  * [S][Hkv][d], 16-byte aligned, pool dtype), go to slot slot_mapping[s]
  * (device int64 [S]) of layer `layer`: block slot / B, offset slot % B, for
  * every key/value head.  A negative slot skips the token; a slot >= P*B is
@@ -263,7 +298,10 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables,
 pa_status pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
                       const int64_t* slot_mapping, int S, hipStream_t stream);
 
-/* copy_blocks: for each pair (src, dst) in pairs (device int32 [N][2]) copy
+/* copy_blocks ("vLLM PagedAttention and continuous batching", section
+ * "Sharing with reference counts and copy-on-write": a write into a shared
+ * block copies that one block first; pa_append_slot emits the pairs): for
+ * each pair (src, dst) in pairs (device int32 [N][2]) copy
  * the whole physical block -- every layer, keys and values, all B slots and
  * Hkv heads -- from src to dst.  Pairs with an id outside [0, P) or src ==
  * dst are skipped.  Destinations must be distinct and must not appear as a
@@ -287,7 +325,9 @@ pa_status pa_swap_blocks(pa_pool* from, pa_pool* to, const int32_t* pairs, int N
 
 /* Workspace for pa_decode_attention calls with up to S sequences, Hq query
  * heads and max_ctx context: split-K partial results (fp32 running maximum,
- * normaliser and weighted value sum per query head and context partition).
+ * normaliser and weighted value sum per query head and context partition:
+ * the state of eq. (4) of "Serving Language Models Within a Memory Budget",
+ * merged by its rescale).
  * The size never decreases with S or max_ctx, so one workspace sized for the
  * largest call serves every smaller one.  Returns 0 for max_ctx == 0 or
  * invalid arguments. */
@@ -299,8 +339,15 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int S, int Hq,
 pa_status pa_decode_workspace_init(void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 
-/* Decode-step paged attention for layer `layer`: for each sequence s and
- * query head h,
+/* Decode-step paged attention for layer `layer` ("vLLM PagedAttention and
+ * continuous batching", sections "PagedAttention: fixed blocks,
+ * non-contiguous physical memory" and "The kernel page": one query token per
+ * sequence reads its blocks through the block table, with the attention
+ * formula unchanged; "Serving Language Models Within a Memory Budget",
+ * section 6 and eq. (4): evaluated block by block with a running maximum and
+ * normaliser, and context partitions merged by the same rescale; "PagedAttention
+ * and Online Inference", section 1: GQA).  For each sequence s and query
+ * head h,
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) V[t]
  * over context positions t = 0..context_lens[s]-1, where K[t], V[t] are key
  * and value head floor(h / (Hq/Hkv)) of slot t % B of physical block
@@ -511,6 +558,24 @@ size_t pa_decode_grouped_workspace_bytes(const pa_pool* pool, int S, int Hq,
  * unsupported. */
 size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq,
                                       int max_ctx, int max_q);
+
+/* Measurement aid: the achievable read rate of decode attention's own
+ * access pattern.  "Serving Language Models Within a Memory Budget",
+ * section 10, asks that the limiting resource be named before a speed is
+ * interpreted; decode attention is bound by reading the cache ("vLLM
+ * PagedAttention and continuous batching", section "How it works"), so this
+ * call reads exactly the key and value rows pa_decode_attention reads --
+ * positions 0 .. context_lens[s]-1 of every sequence and key/value head,
+ * through its block table, in 16-byte loads -- and does no arithmetic but
+ * an XOR of every 32-bit word read:
+ *   checksum[s][h] ^= XOR of all words of key and value rows of sequence s,
+ *                     head h, positions 0 .. context_lens[s]-1.
+ *   checksum : device uint32 [S][Hkv], 4-byte aligned; the caller sets the
+ *              starting value (zero for the plain checksum).
+ * Other arguments, clamping and errors as for pa_decode_attention. */
+pa_status pa_stream_tiles(pa_pool* pool, int layer, const int32_t* block_tables,
+                          int maxb, const int32_t* context_lens, int S,
+                          int max_ctx, uint32_t* checksum, hipStream_t stream);
 
 /* Message describing the calling thread's last failure ("" if none). */
 const char* pa_last_error(void);

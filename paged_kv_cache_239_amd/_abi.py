@@ -81,7 +81,7 @@ HOST_SIGNATURES = {
     "pa_seq_free": (C.c_int, [P, PI32, I32]),
     "pa_seq_reorder": (C.c_int, [P, PI32, PI32, I32, I32, PI32, I32, PI32, PI32]),
     "pa_move_blocks": (C.c_int, [P, P, PI32, PI32, I32, I32, PI32, I32, PI32]),
-    "pa_prefix_groups": (C.c_int, [P, PI32, PI32, I32, I32, PI32, PI32, PI32, PI32, PI32, PI32]),
+    "pa_prefix_groups": (C.c_int, [P, PI32, PI32, I32, I32, PI32, PI32, PI32, PI32, PI32, PI32, PI32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
 }
@@ -111,6 +111,7 @@ DEVICE_SIGNATURES = {
                                                       C.c_float, P, C.c_size_t, P]),
     "pa_decode_grouped_workspace_bytes": (C.c_size_t, [P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                                        C.c_int]),
+    "pa_stream_tiles": (C.c_int, [P, C.c_int, P, C.c_int, P, C.c_int, C.c_int, P, P]),
 }
 
 _libs = {}
@@ -118,10 +119,8 @@ _libs = {}
 
 def load(host_only: bool = False) -> C.CDLL:
     """The product library (libpa.so), or with ``host_only`` the g++ build of
-    the host manager alone (libpa_host.so).  The environment variable
-    PA_LIBRARY names another build of libpa.so (used when sweeping compile-
-    time launch parameters)."""
-    path = HOST_LIB_PATH if host_only else os.environ.get("PA_LIBRARY", LIB_PATH)
+    the host manager alone (libpa_host.so)."""
+    path = HOST_LIB_PATH if host_only else LIB_PATH
     if path in _libs:
         return _libs[path]
     if not os.path.exists(path):

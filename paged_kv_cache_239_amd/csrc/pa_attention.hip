@@ -69,11 +69,6 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest kept weight
 
-// Key/value tiles are read once per step: load them with the streaming
-// (non-temporal) hint so they do not displace reusable lines.
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1
-#endif
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -283,8 +278,6 @@ struct DecodeArgs {
   const int64_t* slots;     // [S] their slots, or null
   int64_t nslots;           // P * B
   int S, Hq, Hkv, P, maxb, max_ctx, part_tokens, nparts_max;
-  int grid_order;           // see decode_attention_kernel
-  int pstride;              // partitions per (sequence, head) in grid order 1
   float scale_log2;         // softmax scale * log2(e)
 };
 
@@ -315,11 +308,6 @@ constexpr int kUnitStepBits = 16;
 template <bool ON> struct UnitList { int unused; };
 template <> struct UnitList<true> { int count; uint32_t unit[kMaxUnits]; };
 
-#ifdef PA_WAVES_PER_EU
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
-#else
-#define PA_OCCUPANCY
-#endif
 
 // QT = 0: one query token per sequence (decode); the G rows are the query
 // heads of one key/value head.  QT > 0: several query tokens per sequence
@@ -332,7 +320,7 @@ template <> struct UnitList<true> { int count; uint32_t unit[kMaxUnits]; };
 // SCHED (one query per sequence): the workgroup's (sequence, partition)
 // comes from the unit list instead of the fixed grid order.
 template <bool BF16, int G, int BS, int NW, int QT, bool SUF = false, bool SCHED = false>
-__global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(const DecodeArgs a,
+__global__ __launch_bounds__(NW * 64) void decode_attention_kernel(const DecodeArgs a,
                                                                                 const UnitList<SCHED> ul) {
   static_assert(!SCHED || (QT == 0 && !SUF), "unit lists order single-query decode launches");
   using SC = Scores<G>;
@@ -346,11 +334,9 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
   constexpr int BPG = BS >= 16 ? 1 : 16 / BS;   // blocks per 16-token step
 
   // 1-D grid; the dispatcher deals consecutive workgroups round-robin to the
-  // 8 XCDs, so the order decides each XCD's share of the work.
-  //   order 0: head fastest -- XCD = head mod 8 when 8 | Hkv, an equal share
-  //            of every sequence for every XCD;
-  //   order 1: partition fastest with an odd partition stride, so the
-  //            partitions of one (sequence, head) spread over all XCDs.
+  // 8 XCDs, so the order decides each XCD's share of the work.  Head fastest:
+  // XCD = head mod 8 when 8 | Hkv, an equal share of every sequence for
+  // every XCD.
   int kvh, s, p, tile = 0;
   {
     const uint32_t id = blockIdx.x;
@@ -367,16 +353,11 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
       t /= a.ntiles;
       s = t % a.S;
       p = t / a.S;
-    } else if (a.grid_order == 0) {
+    } else {
       kvh = id % a.Hkv;
       const uint32_t t = id / a.Hkv;
       s = t % a.S;
       p = t / a.S;
-    } else {
-      p = id % a.pstride;
-      const uint32_t t = id / a.pstride;
-      kvh = t % a.Hkv;
-      s = t / a.Hkv;
     }
   }
   const int lane = threadIdx.x & 63;
@@ -443,8 +424,12 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
     if (t_begin % plen) return;   // not a partition start of this length
     p = t_begin / plen;
   }
-  if (p >= nparts) return;
-  const int t_end = min(n, t_begin + plen);
+  // Suffix pass that stores the output itself (fold): a sequence with no
+  // positions of its own (an empty one) still needs its row written, from
+  // the group partials alone -- partition 0 runs with an empty range.
+  const bool empty_fold = SUF && a.fold && nparts == 0 && p == 0;
+  if (p >= nparts && !empty_fold) return;
+  const int t_end = empty_fold ? t_begin : min(n, t_begin + plen);
 
   __shared__ uint4 s_q[G * 16];
   __shared__ __attribute__((aligned(16))) float s_p[NW][2][4][4 * G];
@@ -542,13 +527,10 @@ __global__ __launch_bounds__(NW * 64) PA_OCCUPANCY void decode_attention_kernel(
       const char* kb = a.kslab + off[(4 * j) / kStepRows] + (uint64_t)((4 * j) % kStepRows) * kRowBytes;
       const char* vb = a.vslab + off[(4 * j) / kStepRows] + (uint64_t)((4 * j) % kStepRows) * kRowBytes;
       if (!tail || tok0 + 4 * j < n) {
-#if PA_NT_LOADS
+        // read once per step: the streaming (non-temporal) hint keeps them
+        // from displacing reusable lines
         K[j] = nt_load16(kb + lane_off);
         V[j] = nt_load16(vb + lane_off);
-#else
-        K[j] = *reinterpret_cast<const uint4*>(kb + lane_off);
-        V[j] = *reinterpret_cast<const uint4*>(vb + lane_off);
-#endif
       } else {
         K[j] = make_uint4(0, 0, 0, 0);
         V[j] = make_uint4(0, 0, 0, 0);
@@ -1479,10 +1461,7 @@ __global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntai
 // ---------------------------------------------------------------------------
 // host-side launch configuration
 // ---------------------------------------------------------------------------
-#ifndef PA_WAVES
-#define PA_WAVES 4
-#endif
-constexpr int kWaves = PA_WAVES;  // waves per workgroup
+constexpr int kWaves = 4;  // waves per workgroup
 
 struct LaunchCfg {
   int part_tokens = 0;
@@ -1504,11 +1483,8 @@ struct LaunchCfg {
 // 100-101 with full partitions plus a remainder at 16-24 steps per wave,
 // and 103-105 at 6-8).
 LaunchCfg choose_launch(int S, int Hkv, int max_ctx, bool ordered = false) {
-  static const int forced = env_int("PA_GROUPS_PER_WAVE", 0);
   int gpw = ordered ? 24 : 12;
-  if (forced > 0) {
-    gpw = forced > 64 ? 64 : forced;   // lanes of a wave hold its groups' blocks
-  } else {
+  {
     // workgroups: 256 CUs x 8 for the fixed grid, whose workgroups past a
     // sequence's end cost little; a unit list holds live units only, and its
     // partitions are worth keeping long down to about one per CU (one GPU's
@@ -1792,10 +1768,7 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   args.ntiles = ntiles;
   args.T = T;
 
-  static const int grid_order = env_int("PA_GRID_ORDER", 0) == 1 ? 1 : 0;
-  args.grid_order = grid_order;
-  args.pstride = cfg.nparts_max | 1;
-  const uint64_t nwg = (uint64_t)pool->Hkv * S * ntiles * (grid_order == 0 || multi ? cfg.nparts_max : args.pstride);
+  const uint64_t nwg = (uint64_t)pool->Hkv * S * ntiles * cfg.nparts_max;
   if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nwg);
   bool ok;
@@ -1856,10 +1829,7 @@ struct GroupedLayout {
 
 // The group pass runs two-wave workgroups: shared prompts are short, and
 // with four waves each would get only a few steps.
-#ifndef PA_GROUP_WAVES
-#define PA_GROUP_WAVES 2
-#endif
-constexpr int kGroupWaves = PA_GROUP_WAVES;
+constexpr int kGroupWaves = 2;
 
 // The suffix pass runs one-wave workgroups (two for G = 8: the kernel stages
 // the query and combines with G * 16 threads): suffixes are short (the tail
@@ -1995,8 +1965,6 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
   args.q_start = group_start;   // the merge finds each group's first member here
   args.ntiles = 1;
   args.T = S;
-  args.grid_order = 0;
-  args.pstride = 1;
   args.grp_len = group_len;
   args.seq_group = seq_group;
   args.ngroups = ngroups;

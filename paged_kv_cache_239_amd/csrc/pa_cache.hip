@@ -99,6 +99,97 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(const char* f
   }
 }
 
+// ---------------------------------------------------------------------------
+// stream_tiles: the key and value rows decode attention reads (positions
+// 0 .. n-1 of every sequence, through its block table), read with the same
+// 16-byte non-temporal loads in the same 16-token steps and no arithmetic
+// but an XOR of every word.  One workgroup of kStreamWaves waves per
+// (sequence, head, partition of kStreamPart positions), head fastest; the
+// waves take the partition's 16-token steps round-robin, a lane holding the
+// physical block of one of its wave's steps.
+// ---------------------------------------------------------------------------
+constexpr int kStreamWaves = 4;
+constexpr int kStreamStepsPerWave = 16;                        // at most 64: one lane per step
+constexpr int kStreamPart = 16 * kStreamWaves * kStreamStepsPerWave;   // 1,024 positions
+
+struct StreamArgs {
+  const char* kslab;
+  const char* vslab;
+  const int32_t* tables;
+  const int32_t* lens;
+  uint32_t* checksum;     // [S][Hkv]
+  uint64_t tile_bytes;
+  int S, Hkv, P, maxb, max_ctx;
+};
+
+template <int BS>
+__global__ __launch_bounds__(kStreamWaves * 64) void stream_tiles_kernel(const StreamArgs a) {
+  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;      // blocks per 16-token step
+  constexpr int kStepRows = BS >= 16 ? 16 : BS;
+  const uint32_t id = blockIdx.x;
+  const int kvh = id % a.Hkv;
+  const uint32_t t = id / a.Hkv;
+  const int s = t % a.S;
+  const int p = t / a.S;
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  n = __builtin_amdgcn_readfirstlane(n);
+  const int t0 = p * kStreamPart;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + kStreamPart);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int g_first = t0 / 16 + wave;                 // this wave's steps: g_first + kStreamWaves * k
+  const int g_end = (t1 + 15) / 16;
+  const int ns = g_first < g_end ? (g_end - g_first + kStreamWaves - 1) / kStreamWaves : 0;
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  int blk[BPG];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    blk[b] = 0;
+    if (lane < ns) {
+      const int idx = ((g_first + kStreamWaves * lane) * 16) / BS + b;
+      const int e = table[idx < a.maxb ? idx : a.maxb - 1];
+      blk[b] = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+    }
+  }
+  const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes + (uint64_t)c * 16;
+  auto load = [&](int k, uint4 (&K)[4], uint4 (&V)[4]) {
+    const int g = g_first + kStreamWaves * k;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = g * 16 + 4 * j + r;
+      const int phys = __builtin_amdgcn_readlane(blk[(4 * j) / kStepRows], k);
+      const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes;
+      if (tok < t1) {
+        K[j] = nt_load16(a.kslab + off);
+        V[j] = nt_load16(a.vslab + off);
+      } else {
+        K[j] = make_uint4(0, 0, 0, 0);
+        V[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  uint32_t x = 0;
+  auto consume = [&](const uint4 (&K)[4], const uint4 (&V)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x ^= K[j].x ^ K[j].y ^ K[j].z ^ K[j].w ^ V[j].x ^ V[j].y ^ V[j].z ^ V[j].w;
+  };
+  uint4 K0[4], V0[4], K1[4], V1[4];
+  if (ns > 0) load(0, K0, V0);
+  for (int k = 0; k < ns; k += 2) {
+    if (k + 1 < ns) load(k + 1, K1, V1);
+    consume(K0, V0);
+    if (k + 2 < ns) load(k + 2, K0, V0);
+    if (k + 1 < ns) consume(K1, V1);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) x ^= __shfl_xor(x, sh);
+  if (lane == 0 && x != 0) atomicXor(a.checksum + (size_t)s * a.Hkv + kvh, x);
+}
+
 // The address at which kernels reach a pool's memory: the memory itself for
 // device memory, the mapped alias for pinned host memory.
 pa_status device_view(const pa_pool* pool, char** out) {
@@ -179,6 +270,45 @@ pa_status pa_swap_blocks(pa_pool* from, pa_pool* to, const int32_t* pairs, int N
   hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, a, b, pairs, from->P, to->P,
                      (uint64_t)from->tile_bytes, (uint64_t)from->slab_bytes, (uint64_t)to->slab_bytes);
   return hip_check(hipGetLastError(), "swap_blocks launch");
+}
+
+pa_status pa_stream_tiles(pa_pool* pool, int layer, const int32_t* block_tables, int maxb,
+                          const int32_t* context_lens, int S, int max_ctx, uint32_t* checksum, hipStream_t stream) {
+  pa_detail::clear_error();
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+  if (S < 0 || maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad S, maxb or max_ctx");
+  if (S == 0 || max_ctx == 0) return PA_OK;
+  if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
+  if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
+  if (!block_tables || !context_lens || !checksum) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(checksum, 4))
+    return fail(PA_ERR_INVALID_ARG, "block_tables, context_lens and checksum must be 4-byte aligned");
+  StreamArgs a;
+  a.kslab = pool->k_slab(layer);
+  a.vslab = pool->v_slab(layer);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.checksum = checksum;
+  a.tile_bytes = pool->tile_bytes;
+  a.S = S;
+  a.Hkv = pool->Hkv;
+  a.P = pool->P;
+  a.maxb = maxb;
+  a.max_ctx = max_ctx;
+  const uint64_t parts = ((uint64_t)max_ctx + kStreamPart - 1) / kStreamPart;
+  const uint64_t nwg = parts * (uint64_t)S * pool->Hkv;
+  if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  const dim3 grid((unsigned)nwg), block(kStreamWaves * 64);
+  switch (pool->B) {
+    case 8: hipLaunchKernelGGL(stream_tiles_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(stream_tiles_kernel<16>, grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(stream_tiles_kernel<32>, grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(stream_tiles_kernel<64>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(stream_tiles_kernel<128>, grid, block, 0, stream, a); break;
+    default: return fail(PA_ERR_UNSUPPORTED, "block size must be 8, 16, 32, 64 or 128");
+  }
+  return hip_check(hipGetLastError(), "stream_tiles launch");
 }
 
 }  // extern "C"

@@ -29,12 +29,6 @@ __device__ __forceinline__ void nt_store16(char* p, const uint4 x) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }
 
-inline int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  return std::atoi(v);
-}
-
 inline pa_status hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return PA_OK;
   return pa_detail::fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));

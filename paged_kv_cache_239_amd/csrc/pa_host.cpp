@@ -511,11 +511,12 @@ pa_status pa_move_blocks(pa_pool* from, pa_pool* to, int32_t* tables, const int3
 
 pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t S, int32_t maxb,
                            int32_t* group_start, int32_t* group_len, int32_t* seq_group, int32_t* n_groups,
-                           int32_t* max_group, int32_t* max_shared) {
+                           int32_t* max_group, int32_t* max_shared, int32_t* max_suffix) {
   pa_detail::clear_error();
   if (pa_status st = check_pool(pool)) return st;
   if (S < 0 || maxb < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
-  if (!n_groups || !max_group || !max_shared || !group_start) return fail(PA_ERR_INVALID_ARG, "NULL output");
+  if (!n_groups || !max_group || !max_shared || !max_suffix || !group_start)
+    return fail(PA_ERR_INVALID_ARG, "NULL output");
   if (S > 0 && (!tables || !lens || !group_len || !seq_group)) return fail(PA_ERR_INVALID_ARG, "NULL array");
   const int B = pool->B;
   for (int32_t s = 0; s < S; ++s)
@@ -523,7 +524,7 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int
   // runs of consecutive sequences with the same first block; a run of one,
   // or one whose shared length rounds to 0, shares nothing.  Consecutive
   // runs that share nothing are joined into one.
-  int32_t ng = 0, mg = 0, ms = 0;
+  int32_t ng = 0, mg = 0, ms = 0, mx = 0;
   int32_t i = 0;
   while (i < S) {
     int32_t j = i + 1;
@@ -552,7 +553,10 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int
       group_len[ng] = L;
       ++ng;
     }
-    for (int32_t m = i; m < j; ++m) seq_group[m] = ng - 1;
+    for (int32_t m = i; m < j; ++m) {
+      seq_group[m] = ng - 1;
+      mx = std::max(mx, lens[m] - L);   // positions outside the shared prefix
+    }
     if (L > 0) {
       mg = std::max(mg, j - i);
       ms = std::max(ms, L);
@@ -563,6 +567,7 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int
   *n_groups = ng;
   *max_group = mg;
   *max_shared = ms;
+  *max_suffix = mx;
   return PA_OK;
 }
 

@@ -138,10 +138,10 @@ class DecodeEngine:
         self.last_slots, self.last_pairs = slots, pairs
         S, mb = self.S, self.maxb
         if self.grouped:
-            gs, gl, sg, self.max_group, self.max_shared = self.pool.prefix_groups(self.tables, self.lens)
+            gs, gl, sg, self.max_group, self.max_shared, self.max_suffix = self.pool.prefix_groups(self.tables,
+                                                                                                   self.lens)
             self.n_groups = len(gl)
-            self.host_group_len = np.asarray(gl, dtype=np.int32).copy()
-            self.max_suffix = int(np.max(self.lens - gl[sg])) if S else 0
+            self.host_group_len = gl
         j, buf = self._staging.next()
         o = 0
         tb = buf[o:o + S * mb * 4]; o += S * mb * 4

@@ -216,18 +216,18 @@ class Pool:
     def prefix_groups(self, tables: np.ndarray, lens):
         """Runs of sequences sharing leading blocks (pa_prefix_groups).
         Returns (group_start int32 [n+1], group_len int32 [n], seq_group int32
-        [S], max_group, max_shared)."""
+        [S], max_group, max_shared, max_suffix)."""
         assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
         S, maxb = tables.shape
         ln = _as_i32(lens)
         gs = np.zeros(S + 1, dtype=np.int32)
         gl = np.zeros(max(S, 1), dtype=np.int32)
         sg = np.zeros(max(S, 1), dtype=np.int32)
-        ng, mg, ms = C.c_int32(), C.c_int32(), C.c_int32()
+        ng, mg, ms, mx = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int32()
         check(self.lib, self.lib.pa_prefix_groups(self.handle, _i32p(tables), _i32p(ln), S, maxb, _i32p(gs), _i32p(gl),
-                                                  _i32p(sg), C.byref(ng), C.byref(mg), C.byref(ms)))
+                                                  _i32p(sg), C.byref(ng), C.byref(mg), C.byref(ms), C.byref(mx)))
         n = ng.value
-        return gs[: n + 1].copy(), gl[:n].copy(), sg[:S].copy(), mg.value, ms.value
+        return gs[: n + 1].copy(), gl[:n].copy(), sg[:S].copy(), mg.value, ms.value, mx.value
 
     def move_blocks(self, to: "Pool", tables: np.ndarray, lens) -> np.ndarray:
         """Swap a group of sequences from this pool to ``to`` (host manager):
@@ -263,6 +263,14 @@ class Pool:
         if N == 0:
             return
         check(self.lib, self.lib.pa_swap_blocks(self.handle, to.handle, _ptr(pairs), N, _stream_handle(stream)))
+
+    def stream_tiles(self, layer: int, block_tables, context_lens, max_ctx: int, checksum, stream=None) -> None:
+        """Read the key/value rows decode attention would read (pa_stream_tiles);
+        checksum: device int32/uint32 [S][Hkv], XORed into."""
+        S = int(context_lens.shape[0])
+        maxb = int(block_tables.shape[1])
+        check(self.lib, self.lib.pa_stream_tiles(self.handle, layer, _ptr(block_tables), maxb, _ptr(context_lens), S,
+                                                 int(max_ctx), _ptr(checksum), _stream_handle(stream)))
 
     def workspace_bytes(self, S: int, Hq: int, max_ctx: int) -> int:
         return int(self.lib.pa_decode_workspace_bytes(self.handle, S, Hq, max_ctx))

@@ -24,3 +24,31 @@ def load_golden(name):
 @pytest.fixture
 def golden():
     return load_golden
+
+
+# The oracle's worker processes for whole-layer parity start before any test
+# initialises the GPU, and only when a selected test asks for them.
+_ORACLE_POOL = None
+
+
+@pytest.hookimpl(trylast=True)     # after marker selection has deselected items
+def pytest_collection_modifyitems(session, config, items):
+    global _ORACLE_POOL
+    if any("oracle_pool" in getattr(item, "fixturenames", ()) for item in items):
+        from oracle.parallel import OraclePool
+        _ORACLE_POOL = OraclePool()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    global _ORACLE_POOL
+    if _ORACLE_POOL is not None:
+        _ORACLE_POOL.close()
+        _ORACLE_POOL = None
+
+
+@pytest.fixture
+def oracle_pool():
+    if _ORACLE_POOL is None:
+        pytest.skip("oracle worker pool not started")
+    return _ORACLE_POOL
+

@@ -1,8 +1,10 @@
 """GPU parity of the HIP path against the fp64 oracle, through the C ABI.
 
 Integer and byte work (slot scatter, block copies, tables, refcounts,
-copy-on-write pairs) must be bit-exact; attention must be within max-abs
-2e-3 and max-rel 1e-2 (relative error over |ref| >= 0.2) of the oracle."""
+copy-on-write pairs) must be bit-exact; attention must be within the stated
+bounds of the oracle: every element within 2e-3 (fp16) or 2e-3 plus half an
+output ulp (bf16, whose rounding alone exceeds 2e-3 above 0.5), and relative
+error at most 1e-2 wherever |ref| >= 0.2."""
 
 import os
 import sys
@@ -19,7 +21,7 @@ from oracle.dtypes import bits_to_f64
 from oracle.replay import build_state, decode_step
 from tests.harness import (OracleSide, fill_pool_nan, fill_pool_random, layer_inputs, make_engine,
                            replay_history_device, snapshot_layers, to_device_bits, to_host_bits,
-                           to_host_f64, tol_stats, within_tolerance)
+                           to_host_f64, tol_stats, within_tolerance, check_prefix_groups)
 from workloads import make_workload, normal_bits, round_to_dtype_bits, with_headroom
 from workloads.gen import dtype_nan_bits
 
@@ -123,7 +125,7 @@ def test_config1_five_lengths_gqa4_b16(fused):
     _say(f"config 1 fused={fused}")
     wl, eng, st, res = _small_workload_step(1, fused=fused)
     got, ref, pairs = res[0]
-    ok, stats = within_tolerance(got, ref)
+    ok, stats = within_tolerance(got, ref, wl.cfg.dtype)
     _say(f"config 1 stats {stats}")
     assert ok, stats
     assert pairs == []
@@ -136,7 +138,7 @@ def test_config2_prefix_sharing_cow(fused):
     _say(f"config 2 fused={fused}")
     wl, eng, st, res = _small_workload_step(2, steps=2, fused=fused)
     for got, ref, pairs in res:
-        ok, stats = within_tolerance(got, ref)
+        ok, stats = within_tolerance(got, ref, wl.cfg.dtype)
         _say(f"config 2 stats {stats}")
         assert ok, stats
     assert len(res[0][2]) == 1 and res[1][2] == []
@@ -176,7 +178,7 @@ def test_config2_isolation_sharers_unchanged():
         slot = t[(lens[s] - 1) // c.B] * c.B + (lens[s] - 1) % c.B
         write_kv(st.pool, 0, wl.knew_bits(0)[s:s + 1], wl.vnew_bits(0)[s:s + 1], [slot])
         ref = decode_layer(st.pool, 0, wl.q_bits(0)[s:s + 1], [t], [lens[s]], float(wl.scale), c.dtype)[0]
-        ok, stats = within_tolerance(got[s], ref)
+        ok, stats = within_tolerance(got[s], ref, c.dtype)
         assert ok, (s, stats)
 
 
@@ -253,7 +255,7 @@ def test_decode_shapes_ragged_lengths(G, Hkv, B, dtype):
     out = _run_direct(pool, tables, q, lens, dtype, scale)
     got = to_host_f64(out, dtype)
     ref = decode_layer(host, 0, q, tables, lens, scale, dtype)
-    ok, stats = within_tolerance(got, ref)
+    ok, stats = within_tolerance(got, ref, dtype)
     _say(f"stats {stats}")
     assert ok, stats
 
@@ -270,7 +272,7 @@ def test_decode_zero_length_gives_zero_and_single_token_gives_value():
     v0 = bits_to_f64(host.V[0, tables[1, 0], :, 0, :], "f16")       # [Hkv][d]
     assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
     ref = decode_layer(host, 0, q[3:4], tables[3:4], [5], 0.1, "f16")
-    assert within_tolerance(got[3], ref[0])[0]
+    assert within_tolerance(got[3], ref[0], "f16")[0]
 
 
 @pytest.mark.parametrize("mag", [30.0, 300.0])
@@ -285,7 +287,7 @@ def test_decode_extreme_logits(mag):
     got = to_host_f64(out, "f16")
     ref = decode_layer(host, 0, q, tables, lens, scale, "f16")
     assert np.all(np.isfinite(got))
-    ok, st = within_tolerance(got, ref)
+    ok, st = within_tolerance(got, ref, "f16")
     _say(f"stats {st}")
     assert ok and st["allclose_worst"] <= 0, st
 
@@ -346,7 +348,7 @@ def test_decode_partition_merge_with_garbage_and_reused_workspace():
         out = torch.empty_like(dq)
         pool.decode_attention(0, out, dq, d_tables, d_lens, max_ctx, scale, workspace=ws)
         torch.cuda.synchronize()
-        ok, stats = within_tolerance(to_host_f64(out, dtype), rr)
+        ok, stats = within_tolerance(to_host_f64(out, dtype), rr, dtype)
         _say(f"{name}: {stats}")
         assert ok, (name, stats)
 
@@ -410,12 +412,12 @@ def test_decode_ordered_matches_oracle_and_fixed_order(fused, case, G, B, dtype)
         assert within_tolerance(to_host_f64(o, dtype)[[s for s, n in enumerate(lens) if n > 0]],
                                 decode_layer(host, 0, q[[s for s, n in enumerate(lens) if n > 0]],
                                              tables[[s for s, n in enumerate(lens) if n > 0]],
-                                             [n for n in lens if n > 0], scale, dtype))[0]
+                                             [n for n in lens if n > 0], scale, dtype), dtype)[0]
     got = to_host_f64(out_ord, dtype)
     live = [s for s, n in enumerate(lens) if n > 0]
     assert np.all(got[[s for s, n in enumerate(lens) if n == 0]] == 0)
     ref = decode_layer(host, 0, q[live], tables[live], [lens[s] for s in live], scale, dtype)
-    ok, stats = within_tolerance(got[live], ref)
+    ok, stats = within_tolerance(got[live], ref, dtype)
     _say(f"stats {stats}")
     assert ok, stats
 
@@ -444,7 +446,7 @@ def test_decode_matches_contiguous_baseline():
     for s, n in enumerate(lens):
         Kc, Vc = gather(host, 0, tables[s], n)
         dense = dense_attention(bits_to_f64(q[s], "f16"), bits_to_f64(Kc, "f16"), bits_to_f64(Vc, "f16"), 0.125)
-        assert within_tolerance(got[s], dense)[0]
+        assert within_tolerance(got[s], dense, "f16")[0]
 
 
 # --------------------------------------------------------------------------------
@@ -481,7 +483,7 @@ def _full_size(cfg, steps, layers, seqs_per_layer, seed, fused=True, block_size=
             pick = sorted(set(pick.tolist()) | {int(np.argmax(lens)), int(np.argmin(lens))})
             for s in pick:
                 ref = ora.expected(layer, s, step)
-                ok, stats = within_tolerance(got_all[s], ref)
+                ok, stats = within_tolerance(got_all[s], ref, c.dtype)
                 assert ok, (cfg, step, layer, s, stats)
                 worst[(step, layer, s)] = stats["max_abs"]
         _say(f"config {cfg} step {step}: pairs={len(pairs)} worst max_abs {max(worst.values()):.2e}")
@@ -539,7 +541,7 @@ def test_small_workloads_at_every_block_size(cfg):
         wl, eng, st, results = _small_workload_step(cfg, steps=2, fused=True, block_size=B)
         outs = []
         for got, ref, pairs in results:
-            ok, stats = within_tolerance(got, ref)
+            ok, stats = within_tolerance(got, ref, wl.cfg.dtype)
             assert ok, (B, stats)
             outs.append(got)
         outs = np.stack(outs)
@@ -732,7 +734,7 @@ def _mq_case(rng, G, Hkv, B, dtype, lens, nqs, ordered=False):
     for s in range(S):
         rows = slice(q_start[s], q_start[s + 1])
         ref = multi_query_one(host, 0, q[rows], tables[s], lens[s], scale, dtype)
-        ok, st = within_tolerance(got[rows], ref)
+        ok, st = within_tolerance(got[rows], ref, dtype)
         assert ok, (s, lens[s], nqs[s], st)
         worst = max(worst, st["max_abs"])
     return worst
@@ -812,7 +814,7 @@ def test_grouped_config2_prefix_sharing(B, fused):
     wl, eng, st, results = _small_workload_step(2, steps=2, fused=fused, block_size=B, grouped=True)
     assert eng.max_shared > 0
     for got, ref, pairs in results:
-        ok, stats = within_tolerance(got, ref)
+        ok, stats = within_tolerance(got, ref, wl.cfg.dtype)
         assert ok, stats
 
 
@@ -829,17 +831,22 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
     `short`, no sequence has more than 128 positions beyond its run's shared
     prefix (members' tails and unshared sequences alike), as in a few steps
     of sampling after a fork."""
-    from oracle.sharing import prefix_groups
     _say(f"grouped direct G={G} B={B} {dtype} short={short}")
     rng = np.random.default_rng(1500 + G + B + (7 if short else 0))
     Hkv, d = 2, 128
     Hq = G * Hkv
     tables, lens = [], []
     nxt = 0
-    groups = [(3, 300), (1, 0), (2, 40), (5, 1100), (1, 0), (1, 0), (4, 17)]
+    # (members, shared prefix); None: an empty sequence (no positions; its
+    # output row must still be written, as zeros)
+    groups = [(3, 300), (1, 0), (2, 40), (5, 1100), (1, 0), (1, None), (1, 0), (4, 17), (1, None)]
     maxb = 0
     plan = []
     for size, prefix in groups:
+        if prefix is None:
+            tables.append([])
+            lens.append(0)
+            continue
         pref_blocks = -(-prefix // B) if prefix else 0
         pref = list(range(nxt, nxt + pref_blocks))
         nxt += pref_blocks
@@ -863,7 +870,7 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
     S = len(lens)
     tab = np.full((S, maxb), 10 ** 6, dtype=np.int32)
     for s_, t in enumerate(tables):
-        tab[s_, :len(t)] = perm[np.array(t)]
+        tab[s_, :len(t)] = perm[np.array(t, dtype=np.int64)]
     from paged_kv_cache_239_amd import Pool
     pool = Pool(1, Hkv, d, B, P, dtype)
     K = normal_bits(rng, (1, P, Hkv, B, d), dtype)
@@ -878,14 +885,12 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
     pool.slab(0, "k").view(torch.int16).copy_(torch.from_numpy(K[0].view(np.int16)))
     pool.slab(0, "v").view(torch.int16).copy_(torch.from_numpy(V[0].view(np.int16)))
     host = HostPool.from_arrays(K, V)
-    gs, gl, sg, mg, ms = pool.prefix_groups(tab, np.array(lens, dtype=np.int32))
-    o_gs, o_gl, o_sg = prefix_groups(tab.tolist(), lens, B)
-    assert gs.tolist() == o_gs and gl.tolist() == o_gl and sg.tolist() == o_sg
+    gs, gl, sg, mg, ms, max_suffix = pool.prefix_groups(tab, np.array(lens, dtype=np.int32))
+    check_prefix_groups(tab.tolist(), lens, B, gs, gl, sg, mg, ms, max_suffix)
     assert ms > 0
     q = round_to_dtype_bits(rng.standard_normal((S, Hq, d)).astype(np.float32), dtype)
     scale = float(np.float32(1 / np.sqrt(d)))
     max_ctx = max(lens)
-    max_suffix = int(max(n - gl[g] for n, g in zip(lens, sg)))
     if short:
         assert max_suffix <= 128 and ms <= 2048
     ws = torch.empty(pool.grouped_workspace_bytes(S, Hq, max_ctx, len(gl), mg, ms, max_suffix), dtype=torch.uint8,
@@ -901,6 +906,106 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
                                       torch.from_numpy(sg).cuda(), mg, ms, max_suffix, scale, ws, host_group_len=hgl)
         torch.cuda.synchronize()
         got = to_host_f64(out, dtype)
-        ok, st = within_tolerance(got, ref)
+        ok, st = within_tolerance(got, ref, dtype)
         _say(f"ordered={hgl is not None} stats {st}")
         assert ok, st
+
+
+# --------------------------------------------------------------------------------
+# streaming-read ceiling kernel: reads exactly attention's key/value rows
+# --------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,Hkv", [(8, 2), (16, 8), (32, 4), (64, 1), (128, 2)])
+def test_stream_tiles_reads_exactly_the_attention_rows(B, Hkv):
+    """The XOR of every 32-bit word pa_stream_tiles reads, per (sequence,
+    head), equals the XOR over the rows of positions 0..n-1 gathered by the
+    oracle through the same tables: no row missed, none read twice, nothing
+    past a sequence's length.  Lengths span several 1,024-position
+    partitions, ragged tails and zero."""
+    from oracle.cache_ops import gather
+    _say(f"stream_tiles B={B} Hkv={Hkv}")
+    rng = np.random.default_rng(4100 + B + Hkv)
+    lens = [0, 1, 15, 16, 17, 1023, 1024, 1025, 2049, 3000, 77]
+    S = len(lens)
+    maxb = -(-max(lens) // B)
+    P = sum(-(-n // B) for n in lens) + 3
+    pool = _pool(1, Hkv, B, P, "bf16")
+    bits = rng.integers(0, 2 ** 16, size=pool.nbytes // 2, dtype=np.uint16)
+    pool.buffer.view(torch.int16).copy_(torch.from_numpy(bits.view(np.int16)))
+    host = HostPool.from_arrays(bits.reshape(1, 2, P, Hkv, B, 128)[:, 0].copy(),
+                                bits.reshape(1, 2, P, Hkv, B, 128)[:, 1].copy())
+    perm = rng.permutation(P)
+    tables = np.full((S, maxb), 10 ** 6, dtype=np.int32)
+    nxt = 0
+    for s, n in enumerate(lens):
+        nb = -(-n // B)
+        tables[s, :nb] = perm[nxt:nxt + nb]
+        nxt += nb
+    chk = torch.zeros((S, Hkv), dtype=torch.int32, device="cuda")
+    pool.stream_tiles(0, torch.from_numpy(tables).cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                      max(lens), chk)
+    torch.cuda.synchronize()
+    got = chk.cpu().numpy().view(np.uint32)
+    for s, n in enumerate(lens):
+        Kc, Vc = gather(host, 0, tables[s], n)             # [n][Hkv][d] uint16
+        for h in range(Hkv):
+            words = np.concatenate([Kc[:, h].reshape(-1).view(np.uint32), Vc[:, h].reshape(-1).view(np.uint32)])
+            want = np.bitwise_xor.reduce(words) if words.size else np.uint32(0)
+            assert got[s, h] == want, (s, n, h)
+
+
+# --------------------------------------------------------------------------------
+# full size, every layer x every sequence of one step (oracle over all host cores)
+# --------------------------------------------------------------------------------
+def _every_layer(cfg, oracle_pool, ordered=True):
+    from oracle.cache_ops import copy_blocks as o_copy, write_kv as o_write
+    from oracle.replay import manager_step
+    wl = with_headroom(make_workload(cfg), 1)
+    c = wl.cfg
+    eng = make_engine(wl, steps=1, ordered=ordered)
+    _say(f"config {cfg} every layer: pool {eng.pool.nbytes / 2**30:.1f} GiB, S={wl.S}, L={c.L}, "
+         f"oracle workers {oracle_pool.workers}")
+    fill_pool_random(eng, wl)
+    replay_history_device(eng, wl, write_values=False)
+    # the oracle's starting slabs: torch's seeded fill, copied before any kernel writes
+    snaps = {l: tuple(eng.pool.slab(l, w).clone() for w in ("k", "v")) for l in range(c.L)}
+    st = build_state(wl, maxb=wl.max_blocks(1))
+    qs, ks, vs = layer_inputs(wl, range(c.L), 0)
+    outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+    max_ctx = eng.manager_step()
+    eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
+    torch.cuda.synchronize()
+    slots, pairs, lens = manager_step(st)
+    assert list(eng.last_slots) == slots and list(eng.lens) == lens
+    assert [tuple(p) for p in eng.last_pairs.tolist()] == pairs
+    worst = 0.0
+    for l in range(c.L):
+        kd, vd = snaps.pop(l)
+        K, V = oracle_pool.layer_buffer(tuple(kd.shape))
+        torch.from_numpy(K.view(np.int16)).copy_(kd.view(torch.int16).cpu())
+        torch.from_numpy(V.view(np.int16)).copy_(vd.view(torch.int16).cpu())
+        del kd, vd
+        hp = HostPool.from_arrays(K[None], V[None])
+        o_copy(hp, pairs)
+        o_write(hp, 0, wl.knew_bits(l, 0), wl.vnew_bits(l, 0), slots)
+        # the device's cache after the step's writes equals the oracle's, byte for byte
+        assert np.array_equal(to_host_bits(eng.pool.slab(l, "k")), K)
+        assert np.array_equal(to_host_bits(eng.pool.slab(l, "v")), V)
+        ref, wall, _ = oracle_pool.decode_layer(wl.q_bits(l, 0), st.tables, st.lens, float(wl.scale), c.dtype)
+        got = to_host_f64(outs[l], c.dtype)
+        ok, stats = within_tolerance(got, ref, c.dtype)
+        assert ok, (cfg, l, stats)
+        worst = max(worst, stats["max_abs"])
+        _say(f"config {cfg} layer {l}: {wl.S} sequences in {wall:.1f} s, max_abs {stats['max_abs']:.2e}")
+    _say(f"config {cfg}: all {c.L} layers x {wl.S} sequences within tolerance, worst max_abs {worst:.2e}")
+    del eng
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_config3_every_layer_every_sequence(oracle_pool):
+    _every_layer(3, oracle_pool)
+
+
+@pytest.mark.timeout(900)
+def test_config4_every_layer_every_sequence(oracle_pool):
+    _every_layer(4, oracle_pool)
