@@ -31,28 +31,34 @@ from .pool import Pool, _ptr, _stream_handle
 
 
 class _Staging:
-    """Ring of pinned host buffers guarded by events, so the host can run a
-    few steps ahead of the device without overwriting a buffer that an
-    earlier asynchronous copy still reads."""
+    """Ring of pinned host buffers guarded by events, so the host can run
+    several steps ahead of the device without overwriting a buffer that an
+    earlier asynchronous copy still reads.
 
-    def __init__(self, nbytes: int, depth: int = 3):
+    The wait for a buffer polls its event: a blocking wait may wake the host
+    milliseconds after the event completes, and with only a few steps queued
+    the device then runs dry (one step in twenty took 8.5 ms instead of
+    3.2 ms).  Eight buffers keep about eight steps of work queued."""
+
+    def __init__(self, nbytes: int, depth: int = 8):
         import torch
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
-        self.events = [None] * depth
+        self.events = [torch.cuda.Event() for _ in range(depth)]
+        self.armed = [False] * depth
         self.i = 0
 
     def next(self):
         j = self.i
         self.i = (self.i + 1) % len(self.bufs)
-        if self.events[j] is not None:
-            self.events[j].synchronize()
+        if self.armed[j]:
+            ev = self.events[j]
+            while not ev.query():
+                pass
         return j, self.bufs[j]
 
     def mark(self, j, stream):
-        import torch
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self.events[j] = ev
+        self.events[j].record(stream)
+        self.armed[j] = True
 
 
 class DecodeEngine:
