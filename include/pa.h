@@ -428,6 +428,31 @@ pa_status pa_decode_attention_ordered(pa_pool* pool, int layer, const void* k,
                                       void* workspace, size_t ws_bytes,
                                       hipStream_t stream);
 
+/* pa_decode_attention_ordered without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The split-K partial
+ * results go to a static device array of the library (32 MiB, one per
+ * device, held until the process ends); the call itself allocates nothing.
+ * Arguments, results and errors as pa_decode_attention_ordered; the output
+ * is bitwise the same as that call's with any large enough workspace.
+ * INVALID_ARG when the launch needs more than 32 MiB of partials (e.g. about
+ * 330 sequences of 4,096 positions at 8 key/value heads and Hq / Hkv = 4);
+ * nothing is launched then.  Every call on one device shares that device's
+ * array, so calls that overlap in time on one device (different streams,
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs to start at zero: every partial a call reads was written by the
+ * same call. */
+pa_status pa_decode_attention_ordered_noalloc(pa_pool* pool, int layer,
+                                              const void* k, const void* v,
+                                              const int64_t* slot_mapping,
+                                              void* out, const void* q, int S,
+                                              int Hq, const int32_t* block_tables,
+                                              int maxb,
+                                              const int32_t* context_lens,
+                                              const int32_t* host_context_lens,
+                                              int max_ctx, float scale,
+                                              hipStream_t stream);
+
 /* Several query tokens per sequence over the same block tables: chunked
  * prefill ("vLLM PagedAttention and continuous batching", section "Chunked
  * prefill": a prefill that does not fit the step's budget is split, each

@@ -98,6 +98,8 @@ DEVICE_SIGNATURES = {
                                                C.c_int, C.c_float, P, C.c_size_t, P]),
     "pa_decode_attention_ordered": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P, P,
                                               C.c_int, C.c_float, P, C.c_size_t, P]),
+    "pa_decode_attention_ordered_noalloc": (C.c_int, [P, C.c_int, P, P, P, P, P, C.c_int, C.c_int, P, C.c_int, P,
+                                                      P, C.c_int, C.c_float, P]),
     "pa_multi_query_attention": (C.c_int, [P, C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, P, C.c_int, P,
                                            C.c_int, C.c_int, C.c_float, P, C.c_size_t, P]),
     "pa_multi_query_attention_ordered": (C.c_int, [P, C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, P, C.c_int,

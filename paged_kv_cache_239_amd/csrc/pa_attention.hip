@@ -58,6 +58,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1556,26 +1557,28 @@ bool dispatch_ordered(int G, const DecodeArgs& args, const UnitList<true>& ul, h
 // zeros) unless `keep_empty` is false.  Workgroups start in id order, so the
 // device stays full until the shortest units, which start last.  Returns
 // the count, or -1 when they do not fit one list.
+// No heap use: a fixed array and an in-place sort whose key (length
+// descending, then position in the list) orders like a stable sort.
 int order_units(const int32_t* host_lens, int S, int max_ctx, int part, UnitList<true>& ul,
                 bool keep_empty = true) {
-  struct U { int len, s, step; };
-  std::vector<U> units;
+  struct U { int len, idx; uint32_t word; };
+  static thread_local U units[kMaxUnits];
+  int cnt = 0;
   for (int s = 0; s < S; ++s) {
     const int n = std::min(std::max(host_lens[s], 0), max_ctx);
     if (n == 0 && !keep_empty) continue;
     const int np = n > 0 ? (n + part - 1) / part : 1;
     const int plen = np > 1 ? ((n + np - 1) / np + 15) / 16 * 16 : part;
     if ((int64_t)n > ((int64_t)1 << kUnitStepBits) * 16 - plen) return -1;
-    for (int p = 0; p < np; ++p) {
-      units.push_back({std::max(std::min(plen, n - p * plen), 0), s, p * plen / 16});
-      if ((int)units.size() > kMaxUnits) return -1;
-    }
+    if (cnt + np > kMaxUnits) return -1;
+    for (int p = 0; p < np; ++p, ++cnt)
+      units[cnt] = {std::max(std::min(plen, n - p * plen), 0), cnt,
+                    ((uint32_t)s << kUnitStepBits) | (uint32_t)(p * plen / 16)};
   }
-  std::stable_sort(units.begin(), units.end(), [](const U& x, const U& y) { return x.len > y.len; });
-  int c = 0;
-  for (const U& u : units) ul.unit[c++] = ((uint32_t)u.s << kUnitStepBits) | (uint32_t)u.step;
-  ul.count = c;
-  return c;
+  std::sort(units, units + cnt, [](const U& x, const U& y) { return x.len != y.len ? x.len > y.len : x.idx < y.idx; });
+  for (int c = 0; c < cnt; ++c) ul.unit[c] = units[c].word;
+  ul.count = cnt;
+  return cnt;
 }
 
 // G query heads per key/value head.  One query per sequence: the rows of a
@@ -1690,7 +1693,7 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
                         const int32_t* block_tables, int maxb, const int32_t* context_lens, int max_ctx, float scale,
                         void* workspace, size_t ws_bytes, const void* k_new, const void* v_new,
                         const int64_t* slot_mapping, const int32_t* q_start, int T, int max_q, hipStream_t stream,
-                        const int32_t* host_lens = nullptr) {
+                        const int32_t* host_lens = nullptr, bool static_scratch = false) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
   if (S < 0) return fail(PA_ERR_INVALID_ARG, "negative S");
@@ -1737,6 +1740,10 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const WsLayout wl = ws_layout(S * ntiles, pool->Hkv, rows, cfg);
   char* ws = static_cast<char*>(workspace);
   if (wl.total > 0) {
+    if (static_scratch && ws_bytes < wl.total)
+      return fail(PA_ERR_INVALID_ARG, "this call needs " + std::to_string(wl.total) +
+                                          " bytes of partial results; the static scratch holds " +
+                                          std::to_string(ws_bytes) + " (use pa_decode_attention_ordered)");
     if (!ws || !aligned(ws, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
     if (ws_bytes < wl.total) return fail(PA_ERR_INVALID_ARG, "workspace smaller than pa_decode_workspace_bytes");
   }
@@ -2020,6 +2027,41 @@ pa_status grouped_launch(pa_pool* pool, int layer, void* out, const void* q, int
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch for pa_decode_attention_ordered_noalloc: the split-K
+// partials live in this file-scope device array instead of a caller's
+// workspace.  Each device that runs the call holds its own copy until the
+// process ends; kernels reach it through the address hipGetSymbolAddress
+// returns on that device (the array's name in host code is only a stand-in).
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+pa_status static_scratch_ptr(void** out) {
+  int dev = -1;
+  if (pa_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (pa_status st = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+      return st;
+    if (!p) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx) {
@@ -2072,6 +2114,27 @@ pa_status pa_decode_attention_ordered(pa_pool* pool, int layer, const void* k, c
   return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, workspace,
                        ws_bytes, fused ? k : nullptr, fused ? v : nullptr, fused ? slot_mapping : nullptr, nullptr, 0,
                        0, stream, host_context_lens);
+}
+
+pa_status pa_decode_attention_ordered_noalloc(pa_pool* pool, int layer, const void* k, const void* v,
+                                              const int64_t* slot_mapping, void* out, const void* q, int S, int Hq,
+                                              const int32_t* block_tables, int maxb, const int32_t* context_lens,
+                                              const int32_t* host_context_lens, int max_ctx, float scale,
+                                              hipStream_t stream) {
+  pa_detail::clear_error();
+  if (S > 0 && !host_context_lens) return fail(PA_ERR_INVALID_ARG, "NULL host_context_lens");
+  const bool fused = k != nullptr || v != nullptr || slot_mapping != nullptr;
+  if (S > 0 && fused) {
+    if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "k, v and slot_mapping must all be given or all NULL");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned, slot_mapping 8-byte aligned");
+  }
+  void* ws = nullptr;
+  if (S > 0)
+    if (pa_status st = static_scratch_ptr(&ws)) return st;
+  return decode_launch(pool, layer, out, q, S, Hq, block_tables, maxb, context_lens, max_ctx, scale, ws,
+                       kStaticScratchBytes, fused ? k : nullptr, fused ? v : nullptr, fused ? slot_mapping : nullptr,
+                       nullptr, 0, 0, stream, host_context_lens, true);
 }
 
 size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq, int max_ctx, int max_q) {

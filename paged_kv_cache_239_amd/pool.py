@@ -385,6 +385,22 @@ class Pool:
             C.c_void_p(ws_ptr or None), C.c_size_t(ws_bytes), _stream_handle(stream)))
 
 
+def decode_attention_ordered_noalloc(pool: Pool, layer: int, out, q, block_tables, context_lens, host_context_lens,
+                                     max_ctx: int, scale: float, k=None, v=None, slot_mapping=None,
+                                     stream=None) -> None:
+    """pa_decode_attention_ordered_noalloc: as Pool.decode_attention_ordered,
+    with the partial results in the library's static device scratch."""
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    maxb = int(block_tables.shape[1])
+    hl = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+    if hl.shape != (S,):
+        raise ValueError("host_context_lens must hold one length per sequence")
+    opt = (lambda t: None if t is None else C.c_void_p(_ptr(t)))
+    check(pool.lib, pool.lib.pa_decode_attention_ordered_noalloc(
+        pool.handle, layer, opt(k), opt(v), opt(slot_mapping), _ptr(out), _ptr(q), S, Hq, _ptr(block_tables), maxb,
+        _ptr(context_lens), hl.ctypes.data, int(max_ctx), C.c_float(scale), _stream_handle(stream)))
+
+
 def multi_query_workspace(pool: Pool, S: int, Hq: int, max_ctx: int, max_q: int, device="cuda", stream=None):
     """A zero-initialised workspace for ``pool.multi_query_attention``."""
     import torch
