@@ -263,6 +263,36 @@ def run(args, opool) -> int:
             snaps_dev[layer] = tuple(eng.pool.slab(layer, w).clone() for w in ("k", "v"))
     torch.cuda.synchronize()
 
+    # Every timing event exists (and has been recorded once) and the collector
+    # has run before the warm-up steps, so that the device idles only for the
+    # final synchronisation between warm-up and timing (after an idle spell
+    # the first launches run slower).
+    hev = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+
+    class _Ev:
+        def __init__(self):
+            self.e = hev.create()
+            hev.record(self.e, sh)
+
+        def record(self, stream=None):
+            hev.record(self.e, sh if stream is None else stream.cuda_stream)
+
+    step_events = [(_Ev(), _Ev()) for _ in range(K)]
+    # one attention call per step is bracketed (a different layer each step):
+    # an event record between two kernels costs a few microseconds, so
+    # bracketing every call would slow the very step being measured
+    attn_pool = [{(7 * i) % c.L: (_Ev(), _Ev())} for i in range(K)]
+    ev0, ev1 = _Ev(), _Ev()
+    torch.cuda.synchronize()
+    attn_events = []
+    alg_bytes = 0
+    attn_alg = []
+    shared = c.length_kind == "lognormal_branches"     # sequences share prompt blocks
+    step_tables = []
+    import gc
+    gc.collect()
+    gc.disable()          # no collector pauses inside the timed region
     fork_step = None
     for w in range(W):
         if w == 0:
@@ -297,33 +327,6 @@ def run(args, opool) -> int:
         eng.device_step(qs, ks, vs, outs, max_ctx, scale)
     torch.cuda.synchronize()
 
-    # every timing event exists (and has been recorded once) before the timed region starts
-    hev = HipEvents()
-    sh = torch.cuda.current_stream().cuda_stream
-
-    class _Ev:
-        def __init__(self):
-            self.e = hev.create()
-            hev.record(self.e, sh)
-
-        def record(self, stream=None):
-            hev.record(self.e, sh if stream is None else stream.cuda_stream)
-
-    step_events = [(_Ev(), _Ev()) for _ in range(K)]
-    # one attention call per step is bracketed (a different layer each step):
-    # an event record between two kernels costs a few microseconds, so
-    # bracketing every call would slow the very step being measured
-    attn_pool = [{(7 * i) % c.L: (_Ev(), _Ev())} for i in range(K)]
-    ev0, ev1 = _Ev(), _Ev()
-    torch.cuda.synchronize()
-    attn_events = []
-    alg_bytes = 0
-    attn_alg = []
-    shared = c.length_kind == "lognormal_branches"     # sequences share prompt blocks
-    step_tables = []
-    import gc
-    gc.collect()
-    gc.disable()          # no collector pauses inside the timed region
     wall0 = time.perf_counter()
     ev0.record()
     issue_ms = []
@@ -765,7 +768,7 @@ def stream_ceiling(eng, c, wl, layers, achieved, grouped) -> dict:
         seq_tables[s, : nb[s]] = np.arange(start, start + nb[s])
         start += int(nb[s])
     out = {"kernel": f"stream_tiles_kernel<B={c.B}>", "kv_bytes_per_launch": kv, "launches": layers}
-    chk = torch.zeros((wl.S, c.Hkv), dtype=torch.int32, device="cuda")
+    chk = torch.zeros(1, dtype=torch.int32, device="cuda")
     max_ctx = int(lens.max())
     for name, tabs in (("shuffled_tables", eng.d_tables), ("consecutive_blocks", torch.from_numpy(seq_tables).cuda())):
         for _ in range(2):      # load the kernel, then time

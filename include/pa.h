@@ -280,6 +280,25 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables,
                            int32_t* max_group, int32_t* max_shared,
                            int32_t* max_suffix);
 
+/* Debug validator of a decode step's device inputs, on the host.  The
+ * kernels trust table entries, lengths and slots for their results (they
+ * only clamp them to stay in bounds), so a caller in debug mode checks them
+ * here first, against the manager's state.  Checks, sequence by sequence:
+ * lens[s] >= 0 and ceil(lens[s] / B) <= maxb; every mapped entry
+ * tables[s][j], j < ceil(lens[s] / B), is a block of the pool that is not
+ * free; no block is mapped by these tables more often than its reference
+ * count ("vLLM PagedAttention and continuous batching", section "Sharing
+ * with reference counts and copy-on-write": the counts are the number of
+ * mappings); and, when slots (host int64 [S]) is given, slots[s] < 0 or it
+ * is the slot of position lens[s]-1 in a block of reference count 1 (the
+ * step's write goes to a private block: any copy-on-write has happened).
+ * Returns INVALID_ARG with the first violation in pa_last_error() and its
+ * sequence in *bad_seq (may be NULL; -1 when the arguments themselves are
+ * bad).  No state changes. */
+pa_status pa_validate_step(const pa_pool* pool, const int32_t* tables,
+                           int32_t maxb, const int32_t* lens, int32_t S,
+                           const int64_t* slots, int32_t* bad_seq);
+
 /* ---------------------------------------------------------------------
  * Device operations ("fused block operations" of the reading guide
  * "Efficient Memory Management for Large Language Model Serving with
@@ -591,13 +610,13 @@ size_t pa_multi_query_workspace_bytes(const pa_pool* pool, int S, int Hq,
  * PagedAttention and continuous batching", section "How it works"), so this
  * call reads exactly the key and value rows pa_decode_attention reads --
  * positions 0 .. context_lens[s]-1 of every sequence and key/value head,
- * through its block table, in 16-byte loads -- and does no arithmetic but
- * an XOR of every 32-bit word read:
- *   checksum[s][h] ^= XOR of all words of key and value rows of sequence s,
- *                     head h, positions 0 .. context_lens[s]-1.
- *   checksum : device uint32 [S][Hkv], 4-byte aligned; the caller sets the
+ * through its block table, in 16-byte loads -- spread evenly over a fixed
+ * grid, and does no arithmetic but an XOR of every 32-bit word read:
+ *   *checksum ^= XOR of all words of the key and value rows read.
+ *   checksum : device uint32 [1], 4-byte aligned; the caller sets the
  *              starting value (zero for the plain checksum).
- * Other arguments, clamping and errors as for pa_decode_attention. */
+ * At most 2,048 sequences (UNSUPPORTED beyond).  Other arguments, clamping
+ * and errors as for pa_decode_attention. */
 pa_status pa_stream_tiles(pa_pool* pool, int layer, const int32_t* block_tables,
                           int maxb, const int32_t* context_lens, int S,
                           int max_ctx, uint32_t* checksum, hipStream_t stream);

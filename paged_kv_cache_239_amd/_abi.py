@@ -82,6 +82,7 @@ HOST_SIGNATURES = {
     "pa_seq_reorder": (C.c_int, [P, PI32, PI32, I32, I32, PI32, I32, PI32, PI32]),
     "pa_move_blocks": (C.c_int, [P, P, PI32, PI32, I32, I32, PI32, I32, PI32]),
     "pa_prefix_groups": (C.c_int, [P, PI32, PI32, I32, I32, PI32, PI32, PI32, PI32, PI32, PI32, PI32]),
+    "pa_validate_step": (C.c_int, [P, PI32, I32, PI32, I32, PI64, PI32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_version": (C.c_char_p, []),
 }

@@ -8,6 +8,8 @@
 //     counts and copy-on-write" (a write into a block that others map
 //     copies that one block first).
 
+#include <atomic>
+
 #include "pa_device_common.h"
 
 using pa_detail::fail;
@@ -101,93 +103,99 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(const char* f
 
 // ---------------------------------------------------------------------------
 // stream_tiles: the key and value rows decode attention reads (positions
-// 0 .. n-1 of every sequence, through its block table), read with the same
-// 16-byte non-temporal loads in the same 16-token steps and no arithmetic
-// but an XOR of every word.  One workgroup of kStreamWaves waves per
-// (sequence, head, partition of kStreamPart positions), head fastest; the
-// waves take the partition's 16-token steps round-robin, a lane holding the
-// physical block of one of its wave's steps.
+// 0 .. n-1 of every sequence and head, through its block table) with the
+// same 16-byte non-temporal loads and no arithmetic but an XOR of every
+// word.  The work item is one mapped block of one sequence: its key tile and
+// value tile of all heads, each Hkv * B * 256 contiguous bytes, read by the
+// workgroup's threads in 4 KiB instructions (rows past the sequence's
+// length skipped).  Items are numbered sequence by sequence and cut into
+// one contiguous, equal range per workgroup, so every workgroup moves the
+// same bytes; a workgroup first builds the prefix of block counts over the
+// sequences in LDS (at most kStreamMaxSeqs), finds its first item by
+// bisection and then walks its range.
 // ---------------------------------------------------------------------------
-constexpr int kStreamWaves = 4;
-constexpr int kStreamStepsPerWave = 16;                        // at most 64: one lane per step
-constexpr int kStreamPart = 16 * kStreamWaves * kStreamStepsPerWave;   // 1,024 positions
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 8;       // 16-byte loads per thread per tile issued together
+constexpr int kStreamMaxSeqs = 2048;   // 16 KiB of LDS for the prefix and lengths
+constexpr int kStreamWgPerCu = 4;
 
 struct StreamArgs {
   const char* kslab;
   const char* vslab;
   const int32_t* tables;
   const int32_t* lens;
-  uint32_t* checksum;     // [S][Hkv]
-  uint64_t tile_bytes;
+  uint32_t* checksum;     // [1]
+  uint64_t tile_bytes;    // Hkv * B * 256: one block of one layer's keys (or values)
   int S, Hkv, P, maxb, max_ctx;
 };
 
 template <int BS>
-__global__ __launch_bounds__(kStreamWaves * 64) void stream_tiles_kernel(const StreamArgs a) {
-  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;      // blocks per 16-token step
-  constexpr int kStepRows = BS >= 16 ? 16 : BS;
-  const uint32_t id = blockIdx.x;
-  const int kvh = id % a.Hkv;
-  const uint32_t t = id / a.Hkv;
-  const int s = t % a.S;
-  const int p = t / a.S;
-  int n = a.lens[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  n = __builtin_amdgcn_readfirstlane(n);
-  const int t0 = p * kStreamPart;
-  if (t0 >= n) return;
-  const int t1 = min(n, t0 + kStreamPart);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane >> 4;
-  const int c = lane & 15;
-  const int g_first = t0 / 16 + wave;                 // this wave's steps: g_first + kStreamWaves * k
-  const int g_end = (t1 + 15) / 16;
-  const int ns = g_first < g_end ? (g_end - g_first + kStreamWaves - 1) / kStreamWaves : 0;
-  const int32_t* table = a.tables + (size_t)s * a.maxb;
-  int blk[BPG];
+__global__ __launch_bounds__(kStreamThreads) void stream_tiles_kernel(const StreamArgs a) {
+  __shared__ int s_pre[kStreamMaxSeqs + 1];   // mapped blocks of sequences 0 .. s-1
+  __shared__ int s_len[kStreamMaxSeqs];
+  const int t = threadIdx.x;
+  if (t < 64) {
+    int carry = 0;
+    for (int base = 0; base < a.S; base += 64) {
+      const int s = base + t;
+      int n = s < a.S ? a.lens[s] : 0;
+      n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+      int v = (n + BS - 1) / BS;
 #pragma unroll
-  for (int b = 0; b < BPG; ++b) {
-    blk[b] = 0;
-    if (lane < ns) {
-      const int idx = ((g_first + kStreamWaves * lane) * 16) / BS + b;
-      const int e = table[idx < a.maxb ? idx : a.maxb - 1];
-      blk[b] = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
-    }
-  }
-  const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes + (uint64_t)c * 16;
-  auto load = [&](int k, uint4 (&K)[4], uint4 (&V)[4]) {
-    const int g = g_first + kStreamWaves * k;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = g * 16 + 4 * j + r;
-      const int phys = __builtin_amdgcn_readlane(blk[(4 * j) / kStepRows], k);
-      const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes;
-      if (tok < t1) {
-        K[j] = nt_load16(a.kslab + off);
-        V[j] = nt_load16(a.vslab + off);
-      } else {
-        K[j] = make_uint4(0, 0, 0, 0);
-        V[j] = make_uint4(0, 0, 0, 0);
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (t >= o) v += y;
       }
+      if (s < a.S) {
+        s_pre[s + 1] = carry + v;
+        s_len[s] = n;
+      }
+      carry += __shfl(v, 63);
     }
-  };
+    if (t == 0) s_pre[0] = 0;
+  }
+  __syncthreads();
+  const int items = s_pre[a.S];
+  const int per_wg = (items + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int i0 = (int)blockIdx.x * per_wg;
+  const int i1 = min(items, i0 + per_wg);
+  if (i0 >= i1) return;
+  int lo = 0, hi = a.S - 1;
+  while (lo < hi) {                   // the sequence holding item i0: last s with s_pre[s] <= i0
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= i0) lo = mid; else hi = mid - 1;
+  }
+  int s = lo;
+  const int nch = (int)(a.tile_bytes / 16);   // 16-byte chunks per tile; chunk k is row (k / 16) % BS
   uint32_t x = 0;
-  auto consume = [&](const uint4 (&K)[4], const uint4 (&V)[4]) {
+  for (int i = i0; i < i1; ++i) {
+    while (s_pre[s + 1] <= i) ++s;
+    const int j = i - s_pre[s];
+    const int rows = min(BS, s_len[s] - j * BS);
+    int e = a.tables[(size_t)s * a.maxb + (j < a.maxb ? j : a.maxb - 1)];
+    e = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+    const char* kb = a.kslab + (uint64_t)e * a.tile_bytes;
+    const char* vb = a.vslab + (uint64_t)e * a.tile_bytes;
+    for (int k0 = t; k0 < nch; k0 += kStreamThreads * kStreamUnroll) {
+      uint4 K[kStreamUnroll], V[kStreamUnroll];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x ^= K[j].x ^ K[j].y ^ K[j].z ^ K[j].w ^ V[j].x ^ V[j].y ^ V[j].z ^ V[j].w;
-  };
-  uint4 K0[4], V0[4], K1[4], V1[4];
-  if (ns > 0) load(0, K0, V0);
-  for (int k = 0; k < ns; k += 2) {
-    if (k + 1 < ns) load(k + 1, K1, V1);
-    consume(K0, V0);
-    if (k + 2 < ns) load(k + 2, K0, V0);
-    if (k + 1 < ns) consume(K1, V1);
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int k = k0 + u * kStreamThreads;
+        K[u] = make_uint4(0, 0, 0, 0);
+        V[u] = make_uint4(0, 0, 0, 0);
+        if (k < nch && ((k >> 4) % BS) < rows) {
+          K[u] = nt_load16(kb + (uint64_t)k * 16);
+          V[u] = nt_load16(vb + (uint64_t)k * 16);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u)
+        x ^= K[u].x ^ K[u].y ^ K[u].z ^ K[u].w ^ V[u].x ^ V[u].y ^ V[u].z ^ V[u].w;
+    }
   }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) x ^= __shfl_xor(x, sh);
-  if (lane == 0 && x != 0) atomicXor(a.checksum + (size_t)s * a.Hkv + kvh, x);
+  if ((t & 63) == 0 && x != 0) atomicXor(a.checksum, x);
 }
 
 // The address at which kernels reach a pool's memory: the memory itself for
@@ -279,11 +287,24 @@ pa_status pa_stream_tiles(pa_pool* pool, int layer, const int32_t* block_tables,
   if (layer < 0 || layer >= pool->L) return fail(PA_ERR_INVALID_ARG, "layer out of range");
   if (S < 0 || maxb <= 0 || max_ctx < 0) return fail(PA_ERR_INVALID_ARG, "bad S, maxb or max_ctx");
   if (S == 0 || max_ctx == 0) return PA_OK;
+  if (S > kStreamMaxSeqs) return fail(PA_ERR_UNSUPPORTED, "at most 2048 sequences");
   if (pool->d != kD) return fail(PA_ERR_UNSUPPORTED, "head dimension must be 128");
   if ((int64_t)max_ctx > (int64_t)maxb * pool->B) return fail(PA_ERR_INVALID_ARG, "max_ctx exceeds maxb * B");
+  if ((int64_t)S * maxb > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many blocks");
   if (!block_tables || !context_lens || !checksum) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(checksum, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables, context_lens and checksum must be 4-byte aligned");
+  static std::atomic<int> cus[64];     // compute units per device, looked up once
+  int dev = 0;
+  if (pa_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_UNSUPPORTED, "device index above 63");
+  if (cus[dev].load() == 0) {
+    int n = 0;
+    if (pa_status st = hip_check(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                                 "hipDeviceGetAttribute"))
+      return st;
+    cus[dev].store(n > 0 ? n : 256);
+  }
   StreamArgs a;
   a.kslab = pool->k_slab(layer);
   a.vslab = pool->v_slab(layer);
@@ -296,10 +317,7 @@ pa_status pa_stream_tiles(pa_pool* pool, int layer, const int32_t* block_tables,
   a.P = pool->P;
   a.maxb = maxb;
   a.max_ctx = max_ctx;
-  const uint64_t parts = ((uint64_t)max_ctx + kStreamPart - 1) / kStreamPart;
-  const uint64_t nwg = parts * (uint64_t)S * pool->Hkv;
-  if (nwg > 0x7fffffffULL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
-  const dim3 grid((unsigned)nwg), block(kStreamWaves * 64);
+  const dim3 grid((unsigned)(cus[dev].load() * kStreamWgPerCu)), block(kStreamThreads);
   switch (pool->B) {
     case 8: hipLaunchKernelGGL(stream_tiles_kernel<8>, grid, block, 0, stream, a); break;
     case 16: hipLaunchKernelGGL(stream_tiles_kernel<16>, grid, block, 0, stream, a); break;

@@ -22,6 +22,7 @@
 #include <limits>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -568,6 +569,47 @@ pa_status pa_prefix_groups(const pa_pool* pool, const int32_t* tables, const int
   *max_group = mg;
   *max_shared = ms;
   *max_suffix = mx;
+  return PA_OK;
+}
+
+pa_status pa_validate_step(const pa_pool* pool, const int32_t* tables, int32_t maxb, const int32_t* lens, int32_t S,
+                           const int64_t* slots, int32_t* bad_seq) {
+  pa_detail::clear_error();
+  if (pa_status st = check_pool(pool)) return st;
+  if (bad_seq) *bad_seq = -1;
+  if (S < 0 || maxb <= 0) return fail(PA_ERR_INVALID_ARG, "negative S or maxb below 1");
+  if (S > 0 && (!tables || !lens)) return fail(PA_ERR_INVALID_ARG, "NULL array");
+  const int B = pool->B;
+  auto bad = [&](int32_t s, const std::string& what) {
+    if (bad_seq) *bad_seq = s;
+    return fail(PA_ERR_INVALID_ARG, "sequence " + std::to_string(s) + ": " + what);
+  };
+  std::vector<int32_t> held((size_t)pool->P, 0);   // references these tables hold
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t n = lens[s];
+    if (n < 0) return bad(s, "negative length");
+    const int64_t nb = ((int64_t)n + B - 1) / B;
+    if (nb > maxb) return bad(s, "length " + std::to_string(n) + " needs more than maxb entries");
+    const int32_t* t = tables + (size_t)s * maxb;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = t[j];
+      if (!in_range(pool, b)) return bad(s, "entry " + std::to_string(j) + " = " + std::to_string(b) + " outside the pool");
+      if (pool->ref[(size_t)b] <= 0) return bad(s, "entry " + std::to_string(j) + " maps free block " + std::to_string(b));
+      if (++held[(size_t)b] > pool->ref[(size_t)b])
+        return bad(s, "block " + std::to_string(b) + " is mapped more often than its reference count");
+    }
+    if (slots) {
+      const int64_t slot = slots[s];
+      if (slot < 0) continue;
+      if (n < 1) return bad(s, "a slot for an empty sequence");
+      const int32_t b = t[(n - 1) / B];
+      const int64_t want = (int64_t)b * B + (n - 1) % B;
+      if (slot != want)
+        return bad(s, "slot " + std::to_string(slot) + " is not position n-1 (" + std::to_string(want) + ")");
+      if (pool->ref[(size_t)b] != 1)
+        return bad(s, "the written block " + std::to_string(b) + " is shared (copy-on-write missing)");
+    }
+  }
   return PA_OK;
 }
 

@@ -64,10 +64,13 @@ class _Staging:
 class DecodeEngine:
     def __init__(self, L: int, Hq: int, Hkv: int, d: int, B: int, P: int, dtype: str, S: int, maxb: int,
                  free_order: Optional[Sequence[int]] = None, device: str = "cuda", fused: bool = True,
-                 grouped: bool = False, ordered: bool = True):
+                 grouped: bool = False, ordered: bool = True, debug: bool = False):
         import torch
         self.torch = torch
         self.fused = fused
+        # check every step's tables, lengths and slots against the manager
+        # (pa_validate_step) before they are uploaded
+        self.debug = debug
         # launch the context partitions longest first from the manager's own
         # lengths (pa_decode_attention_ordered)
         self.ordered = ordered
@@ -142,6 +145,8 @@ class DecodeEngine:
         slots, pairs = self.pool.append_batch(self.tables, n_before)
         self.lens += 1
         self.last_slots, self.last_pairs = slots, pairs
+        if self.debug:
+            self.pool.validate_step(self.tables, self.lens, slots)
         S, mb = self.S, self.maxb
         if self.grouped:
             gs, gl, sg, self.max_group, self.max_shared, self.max_suffix = self.pool.prefix_groups(self.tables,

@@ -229,6 +229,22 @@ class Pool:
         n = ng.value
         return gs[: n + 1].copy(), gl[:n].copy(), sg[:S].copy(), mg.value, ms.value, mx.value
 
+    def validate_step(self, tables: np.ndarray, lens, slots=None) -> None:
+        """Debug check of a step's tables, lengths and slots against the
+        manager (pa_validate_step); raises PAError naming the first bad
+        sequence (attribute ``bad_seq``)."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.ndim == 2
+        S, maxb = tables.shape
+        ln = _as_i32(lens)
+        sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int64)
+        bad = C.c_int32(-1)
+        st = self.lib.pa_validate_step(self.handle, _i32p(tables), maxb, _i32p(ln), S,
+                                       None if sl is None else _i64p(sl), C.byref(bad))
+        if st != _abi.PA_OK:
+            err = _abi.PAError(st, self.lib.pa_last_error().decode(errors="replace"))
+            err.bad_seq = bad.value
+            raise err
+
     def move_blocks(self, to: "Pool", tables: np.ndarray, lens) -> np.ndarray:
         """Swap a group of sequences from this pool to ``to`` (host manager):
         ``tables`` (int32 [S][maxb]) are rewritten in place to name blocks of
@@ -266,7 +282,7 @@ class Pool:
 
     def stream_tiles(self, layer: int, block_tables, context_lens, max_ctx: int, checksum, stream=None) -> None:
         """Read the key/value rows decode attention would read (pa_stream_tiles);
-        checksum: device int32/uint32 [S][Hkv], XORed into."""
+        checksum: device int32/uint32 [1], XORed into."""
         S = int(context_lens.shape[0])
         maxb = int(block_tables.shape[1])
         check(self.lib, self.lib.pa_stream_tiles(self.handle, layer, _ptr(block_tables), maxb, _ptr(context_lens), S,

@@ -916,11 +916,11 @@ def test_grouped_direct_random_runs(G, B, dtype, short):
 # --------------------------------------------------------------------------------
 @pytest.mark.parametrize("B,Hkv", [(8, 2), (16, 8), (32, 4), (64, 1), (128, 2)])
 def test_stream_tiles_reads_exactly_the_attention_rows(B, Hkv):
-    """The XOR of every 32-bit word pa_stream_tiles reads, per (sequence,
-    head), equals the XOR over the rows of positions 0..n-1 gathered by the
-    oracle through the same tables: no row missed, none read twice, nothing
-    past a sequence's length.  Lengths span several 1,024-position
-    partitions, ragged tails and zero."""
+    """The XOR of every 32-bit word pa_stream_tiles reads equals the XOR over
+    the rows of positions 0..n-1 that the oracle gathers through the same
+    tables (a row missed or read twice would change it), and each sequence's
+    rows alone give that sequence's XOR (a call per sequence).  Lengths span
+    ragged tails, zero and several thousand positions."""
     from oracle.cache_ops import gather
     _say(f"stream_tiles B={B} Hkv={Hkv}")
     rng = np.random.default_rng(4100 + B + Hkv)
@@ -940,17 +940,25 @@ def test_stream_tiles_reads_exactly_the_attention_rows(B, Hkv):
         nb = -(-n // B)
         tables[s, :nb] = perm[nxt:nxt + nb]
         nxt += nb
-    chk = torch.zeros((S, Hkv), dtype=torch.int32, device="cuda")
-    pool.stream_tiles(0, torch.from_numpy(tables).cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"),
-                      max(lens), chk)
-    torch.cuda.synchronize()
-    got = chk.cpu().numpy().view(np.uint32)
+    want_seq = []
     for s, n in enumerate(lens):
         Kc, Vc = gather(host, 0, tables[s], n)             # [n][Hkv][d] uint16
-        for h in range(Hkv):
-            words = np.concatenate([Kc[:, h].reshape(-1).view(np.uint32), Vc[:, h].reshape(-1).view(np.uint32)])
-            want = np.bitwise_xor.reduce(words) if words.size else np.uint32(0)
-            assert got[s, h] == want, (s, n, h)
+        words = np.concatenate([Kc.reshape(-1).view(np.uint32), Vc.reshape(-1).view(np.uint32)])
+        want_seq.append(int(np.bitwise_xor.reduce(words)) if words.size else 0)
+    want_all = 0
+    for w in want_seq:
+        want_all ^= w
+    d_tab = torch.from_numpy(tables).cuda()
+    d_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    chk = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool.stream_tiles(0, d_tab, d_len, max(lens), chk)
+    torch.cuda.synchronize()
+    assert int(chk.cpu().numpy().view(np.uint32)[0]) == want_all
+    for s, n in enumerate(lens):
+        one = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pool.stream_tiles(0, d_tab[s:s + 1], d_len[s:s + 1], max(n, 1), one)
+        torch.cuda.synchronize()
+        assert int(one.cpu().numpy().view(np.uint32)[0]) == want_seq[s], (s, n)
 
 
 # --------------------------------------------------------------------------------
@@ -1009,3 +1017,43 @@ def test_config3_every_layer_every_sequence(oracle_pool):
 @pytest.mark.timeout(900)
 def test_config4_every_layer_every_sequence(oracle_pool):
     _every_layer(4, oracle_pool)
+
+
+def test_config5_fork_step_cow_sources_unchanged_debug_engine():
+    """The fork step of the parallel-sampling workload with the engine in
+    debug mode (pa_validate_step on every step): after the copies and the
+    fused writes, every copy-on-write source block is bitwise unchanged in
+    every layer, and every copy equals its source except the one row per
+    (layer, key or value, head) that the step writes -- the new token's."""
+    _say("config 5 fork step, debug engine, copy-on-write sources")
+    wl = with_headroom(make_workload(5), 1)
+    c = wl.cfg
+    eng = make_engine(wl, steps=1, grouped=True)
+    eng.debug = True
+    fill_pool_random(eng, wl)
+    replay_history_device(eng, wl, write_values=False)
+    qs, ks, vs = layer_inputs(wl, range(c.L), 0)
+    outs = {l: torch.empty_like(qs[l]) for l in range(c.L)}
+    max_ctx = eng.manager_step()
+    pairs = eng.last_pairs.copy()
+    assert len(pairs) > 100
+    tile = eng.pool.nbytes // (2 * c.L * wl.P)
+    view = eng.pool.buffer.view(2 * c.L, wl.P, tile)
+    src_idx = torch.from_numpy(pairs[:, 0].astype(np.int64)).cuda()
+    dst_idx = torch.from_numpy(pairs[:, 1].astype(np.int64)).cuda()
+    before = view.index_select(1, src_idx).clone()
+    eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
+    torch.cuda.synchronize()
+    assert torch.equal(view.index_select(1, src_idx), before)
+    # the copies: equal to the source but for the written row of each head
+    row = c.d * 2
+    dst = view.index_select(1, dst_idx).view(2 * c.L, len(pairs), c.Hkv, c.B, row)
+    src = before.view(2 * c.L, len(pairs), c.Hkv, c.B, row)
+    slot_of = {}
+    for s, slot in enumerate(eng.last_slots.tolist()):
+        slot_of[int(slot) // c.B] = int(slot) % c.B
+    diff = (dst != src).any(dim=-1).any(dim=0).any(dim=1).cpu().numpy()      # [pairs][B]: rows that changed
+    for i, (a, b) in enumerate(pairs.tolist()):
+        changed = np.nonzero(diff[i])[0].tolist()
+        assert changed == [slot_of[b]], (a, b, changed)
+    _say(f"{len(pairs)} copies checked over {c.L} layers")
