@@ -584,7 +584,9 @@ def multi_query_bench(args) -> int:
                                f"(context {int(wl.lengths0.min()) - 1}..{int(wl.lengths0.max()) - 1} before the first step)",
                    "queries_per_sequence": Q, "block_size": c.B, "layers": c.L},
         "query_tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": (f"mq_mfma_kernel<{c.dtype},G={c.G},B={c.B}> + merge" if mfma else
+        "roofline": {"kernel": (f"mq_wide_kernel<{c.dtype},G={c.G},B={c.B}> (whole context per workgroup, no merge)"
+                                if Q * c.G > 32 else
+                                f"mq_mfma_kernel<{c.dtype},G={c.G},B={c.B}> + merge" if mfma else
                                 f"decode_attention_kernel<{c.dtype},rows=8,B={c.B},QT={8 // c.G}> + merge"),
                      "bound": "hbm" if mem_bound else ("mfma" if mfma else "alu"),
                      "achieved": round(gbs, 1) if mem_bound else round(tfs, 2),

@@ -1233,223 +1233,292 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
   }
 }
 
-// Many rows per sequence (a chunk of a split prefill): each of the NW waves
-// owns 16 different rows (16 NW per workgroup) and all waves walk the same
-// 16-token steps.  The workgroup loads each key and value tile once into LDS
-// (double-buffered, one barrier per step) and every wave computes its rows
-// from there: K as the A operand read back row-major (272-byte stride:
-// conflict-free 16-byte reads), V transposed as in mq_mfma_kernel.  A wave
-// finishes its rows alone; no cross-wave combine.
-template <bool BF16, int GQ, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void mq_mfma_rows_kernel(
-    const DecodeArgs a) {
-  constexpr int R = 16 * NW;        // rows per workgroup
-  constexpr int QT = R / GQ;        // query tokens per workgroup
-  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
-  constexpr int BPG = BS >= 16 ? 1 : 16 / BS;
-  static_assert(NW * 64 == 256, "one 16-byte key load and one value load per thread per step");
+// Many rows per sequence (a chunk of a split prefill): one workgroup takes
+// up to 64 RT rows of a (sequence, key/value head) -- query tokens x query
+// heads -- and walks the sequence's whole context once, so there are no
+// partial results to merge; further row tiles of the same sequence and head
+// are further workgroups, dealt to the same XCD (head fastest in the grid),
+// whose reads of the context mostly hit its L2.  Four waves own RT 16-row
+// tiles each (wave w: rows 16 RT w ..);
+// all waves share the 32-token steps, staged by the workgroup in a ring of
+// four LDS buffers (three steps in flight, one barrier per step).  Per step
+// and row tile, on the matrix cores (16x16x32 for both products):
+//   S^T[token][row] = K[token][:] . Q[row][:] for the step's two 16-token
+//       halves h: A = K rows of half h (lane: token lane % 16, dims
+//       32 ks + 8 kq .. +7, read from LDS), B = Q^T held in registers; lane
+//       (row, kq) gets the scores of tokens 16 h + 4 kq .. +3 of its row;
+//   O^T[dim][row] += V^T[dim][token] . P^T[token][row] with the step's 32
+//       tokens ordered so that lane (row, kq) supplies exactly its own eight
+//       probabilities (tokens 4 kq .. +3 and 16 + 4 kq .. +3) as B; A = V^T in
+//       the same token order, gathered from the row-major LDS value tile;
+//       lane (row, kq) accumulates dims 16 nb + 4 kq .. +3 of its row.
+// The row's running maximum and normaliser live in the four lanes of the
+// row (one per kq); bf16 probabilities enter P.V as a rounded part plus the
+// rounded remainder (two products), fp16 ones as one.
+constexpr int kWideTok = 32;                    // tokens per step
+constexpr int kWideBufs = 4;                    // LDS ring: steps k .. k+3
+constexpr int kWideRow = 272;                   // LDS bytes per token row (256 + 16 pad)
+constexpr int kWideTabMax = 2048;               // table entries cached in LDS
 
-  int kvh, s, p, tile;
+
+template <bool BF16, int GQ, int BS, int RT, bool SCHED>
+__global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const UnitList<SCHED> ul) {
+  constexpr int NW = 4;
+  constexpr int R = 16 * RT * NW;                 // rows per workgroup
+  constexpr int QT = R / GQ;                      // query tokens per workgroup
+  static_assert(QT * GQ == R, "rows = query tokens x query heads");
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
+
+  int kvh, s, tile;
   {
-    const uint32_t id = blockIdx.x;   // head, then query tile, sequence, partition
+    const uint32_t id = blockIdx.x;               // head, then row tile, then sequence
     kvh = id % a.Hkv;
     uint32_t t = id / a.Hkv;
     tile = t % a.ntiles;
     t /= a.ntiles;
-    s = t % a.S;
-    p = t / a.S;
+    if constexpr (SCHED) {                        // sequences longest first
+      s = (int)ul.unit[min(t, (uint32_t)kMaxUnits - 1)];
+    } else {
+      s = (int)t;
+    }
+    if (s >= a.S) return;
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane & 15;
   const int kq = lane >> 4;
-  const int wrow = wave * 16 + row;  // row of the workgroup
 
-  const int t_begin = p * a.part_tokens;
-  const int step0 = t_begin / 16;
-  const int32_t* table = a.tables + (size_t)s * a.maxb;
-  int entry[BPG];
-#pragma unroll
-  for (int b = 0; b < BPG; ++b) {
-    const int idx = ((step0 + lane) * 16) / BS + b;   // lane k: the block of step k
-    entry[b] = table[idx < a.maxb ? idx : a.maxb - 1];
-  }
   const int q0 = min(max(a.q_start[s], 0), a.T);
-  int nq = min(max(a.q_start[s + 1], q0), a.T) - q0;
-  const int tq = tile * QT + wrow / GQ;
-  uint4 qb[4];
-  {
+  const int nq = __builtin_amdgcn_readfirstlane(min(max(a.q_start[s + 1], q0), a.T) - q0);
+  int n = a.lens[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (tile * QT >= nq || nq > n) return;
+  // positions the workgroup reads: up to what its last query sees
+  const int n_wg = n - nq + min(tile * QT + QT, nq);
+  const int nsteps = (n_wg + kWideTok - 1) / kWideTok;
+
+  // query rows of this wave: Q^T operands, and each row tile's visible limit
+  uint4 qb[RT][4];
+  int lim[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int wrow = (wave * RT + rt) * 16 + row;     // row of the workgroup
+    const int tq = tile * QT + wrow / GQ;
     const bool live = tq < nq;
+    lim[rt] = live ? n - nq + tq + 1 : 0;
     const uint4* qrow = reinterpret_cast<const uint4*>(
         a.q + ((size_t)(live ? q0 + tq : 0) * a.Hq + (size_t)kvh * GQ + wrow % GQ) * kD);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) qb[rt][ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
   }
-
-  int n = a.lens[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  nq = __builtin_amdgcn_readfirstlane(nq);
-  if (tile * QT >= nq || nq > n) return;
-  const int lim_min = n - nq + tile * QT + 1;
-  n = __builtin_amdgcn_readfirstlane(n - nq + min(tile * QT + QT, nq));
-  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
-  if (p >= nparts) return;
-  const int t_end = min(n, t_begin + a.part_tokens);
-  const int nsteps = (t_end - t_begin + 15) / 16;       // at most 64 (host-side limit)
-  const int lim = tq < nq ? lim_min + wrow / GQ : 0;
-  int my_phys[BPG];
+  // the first position some row of this wave cannot see: steps before it need no mask
+  int wave_lim_min;
+  {
+    // the smallest limit over the wave's live rows (dead rows have limit 0)
+    int v = 0x7fffffff;
 #pragma unroll
-  for (int b = 0; b < BPG; ++b) {
-    my_phys[b] = 0;
-    if (lane < nsteps) my_phys[b] = entry[b] < 0 ? 0 : (entry[b] >= a.P ? a.P - 1 : entry[b]);
+    for (int rt = 0; rt < RT; ++rt) if (lim[rt] > 0) v = min(v, lim[rt]);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) v = min(v, __shfl_xor(v, sh));
+    wave_lim_min = __builtin_amdgcn_readfirstlane(v);
   }
 
-  // three tile buffers: step k's values, step k+1's keys (scored ahead) and
-  // step k+2 (being stored) are all live during step k
-  __shared__ __attribute__((aligned(16))) char s_k[3][16 * kKRow];
-  __shared__ __attribute__((aligned(16))) char s_v[3][16 * kVRow];
+  // LDS ring of step tiles, keys and values both row-major [token][dim]
+  __shared__ __attribute__((aligned(16))) char s_k[kWideBufs][kWideTok * kWideRow];
+  __shared__ __attribute__((aligned(16))) char s_v[kWideBufs][kWideTok * kWideRow];
+  // the sequence's table row (physical blocks, clamped into the pool)
+  __shared__ int s_tab[kWideTabMax];
 
-  // this thread's share of a step: token lt = tid / 16, 16 bytes at dims 8 lc
+  // this thread's share of a step: tokens lt and lt + 16, 16 bytes at dims 8 lc
   const int lt = tid >> 4;
   const int lc = tid & 15;
   const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
-  auto load_step = [&](int k, uint4& Kx, uint4& Vx) {
-    const int tok = (step0 + k) * 16 + lt;
-    int phys = __builtin_amdgcn_readlane(my_phys[0], k);
-    if constexpr (BPG == 2) {
-      const int phys1 = __builtin_amdgcn_readlane(my_phys[1], k);
-      phys = lt < 8 ? phys : phys1;
+  const int32_t* table = a.tables + (size_t)s * a.maxb;
+  const int nblk = (n_wg + BS - 1) / BS;
+  const bool tab_lds = nblk <= kWideTabMax;    // else blocks come from the table in memory
+  if (tab_lds) {
+    for (int i = tid; i < nblk; i += 256) {
+      const int e = table[i < a.maxb ? i : a.maxb - 1];
+      s_tab[i] = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
     }
-    const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + lc * 16;
-    if (tok < n) {
-      Kx = nt_load16(a.kslab + off);
-      Vx = nt_load16(a.vslab + off);
-    } else {
-      Kx = make_uint4(0, 0, 0, 0);
-      Vx = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_step = [&](int b, const uint4& Kx, const uint4& Vx) {
-    *reinterpret_cast<uint4*>(s_k[b] + lt * kKRow + lc * 16) = Kx;
-    *reinterpret_cast<uint4*>(s_v[b] + ((lt & 3) * 4 + (lt >> 2)) * kVRow + lc * 16) = Vx;
-  };
-
-  float m = -INFINITY;
-  float ell = 0.0f;
-  f32x4_t acc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // scores of the step in buffer bb: A = K[token row][dims 32ks + 8kq ..]
-  // from LDS, B = Q^T
-  auto scores = [&](int bb) {
-    f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 kx = *reinterpret_cast<const uint4*>(s_k[bb] + row * kKRow + (32 * ks + 8 * kq) * 2);
-      st = mfma_k32<BF16>(kx, qb[ks], st);
-    }
-    return st;
-  };
-
-  // Software pipeline: step k+1's score products are issued before step k's
-  // softmax, so the matrix cores work while the vector units do.
-  uint4 Kn, Vn;
-  load_step(0, Kn, Vn);
-  store_step(0, Kn, Vn);
-  if (nsteps > 1) {
-    load_step(1, Kn, Vn);
-    store_step(1, Kn, Vn);
   }
-  if (nsteps > 2) load_step(2, Kn, Vn);
   __syncthreads();
-  f32x4_t st = scores(0);
-  int b = 0;   // buffer of step k; k + 1 is in b1, k + 2 goes to b2
+  // Every iteration issues the same four 16-byte loads (the step index and
+  // the position are clamped, rows past n_wg are zeroed when stored), so the
+  // compiler's wait before a store covers exactly the oldest stage.
+  auto load_step = [&](int k, uint4 (&Kx)[2], uint4 (&Vx)[2]) {
+    const int kc = min(k, nsteps - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = min(kc * kWideTok + lt + 16 * j, n_wg - 1);
+      int phys;
+      if (tab_lds) {
+        phys = s_tab[tok / BS];
+      } else {
+        const int e = table[tok / BS];
+        phys = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+      }
+      const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + lc * 16;
+      Kx[j] = nt_load16(a.kslab + off);
+      Vx[j] = nt_load16(a.vslab + off);
+    }
+  };
+  auto store_step = [&](int k, const uint4 (&Kx)[2], const uint4 (&Vx)[2]) {
+    const int bb = k % kWideBufs;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // component-wise selects: a select of whole vector structs goes through memory
+      const uint32_t keep = k * kWideTok + lt + 16 * j < n_wg ? 0xffffffffu : 0u;
+      const uint4 kx = make_uint4(Kx[j].x & keep, Kx[j].y & keep, Kx[j].z & keep, Kx[j].w & keep);
+      const uint4 vx = make_uint4(Vx[j].x & keep, Vx[j].y & keep, Vx[j].z & keep, Vx[j].w & keep);
+      *reinterpret_cast<uint4*>(s_k[bb] + (lt + 16 * j) * kWideRow + lc * 16) = kx;
+      *reinterpret_cast<uint4*>(s_v[bb] + (lt + 16 * j) * kWideRow + lc * 16) = vx;
+    }
+  };
+
+  float m[RT], ell[RT];
+  f32x4_t acc[RT][8];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    ell[rt] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[rt][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // prologue: steps 0 .. 2 in LDS, step 3 in registers
+  uint4 Kn[2], Vn[2];
+#pragma unroll
+  for (int k = 0; k < kWideBufs - 1; ++k) {
+    load_step(k, Kn, Vn);
+    store_step(k, Kn, Vn);
+  }
+  load_step(kWideBufs - 1, Kn, Vn);
+  __syncthreads();
+
+  // scores of the step in buffer b: two 16-token halves x RT row tiles
+  auto scores = [&](int b, f32x4_t (&sc)[RT][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 kx[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kx[ks] = *reinterpret_cast<const uint4*>(s_k[b] + (16 * h + row) * kWideRow + (32 * ks + 8 * kq) * 2);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) st = mfma_k32<BF16>(kx[ks], qb[rt][ks], st);
+        sc[rt][h] = st;
+      }
+    }
+  };
+
+  // (Issuing step k+1's score products before step k's softmax, a deeper
+  // register prefetch, values staged transposed and four row tiles per wave
+  // at one wave per SIMD were all slower at 64 queries per sequence.)
+  f32x4_t sc[RT][2];
+  scores(0, sc);
   for (int k = 0; k < nsteps; ++k) {
-    const int b1 = b == 2 ? 0 : b + 1;
-    const int b2 = b1 == 2 ? 0 : b1 + 1;
-    const int tok0 = (step0 + k) * 16;
-    f32x4_t st_next = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    if (k + 1 < nsteps) st_next = scores(b1);
-    float sc[4];
-    float mx = -INFINITY;
+    const int bb = k % kWideBufs;
+    const int tok0 = k * kWideTok;
+    const bool edge = tok0 + kWideTok > wave_lim_min;   // some row of the wave stops inside this step
+    // online softmax per row tile; probabilities in the storage type
+    uint4 pb[RT], pl[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = st[i] * a.scale_log2;
-      if (tok0 + 4 * kq + i >= lim) sc[i] = -INFINITY;
-      mx = fmaxf(mx, sc[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float f = (m_new == m) ? 1.0f : exp2_fast(m - m_new);
-      m = m_new;
-      ell *= f;
+    for (int rt = 0; rt < RT; ++rt) {
+      float x[8];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[nb] *= f;
-    }
-    float pe[4];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pe[i] = (sc[i] == -INFINITY) ? 0.0f : exp2_fast(sc[i] - m);
-      ell += pe[i];
+        for (int i = 0; i < 4; ++i) {
+          float v = sc[rt][h][i] * a.scale_log2;
+          if (edge && tok0 + 16 * h + 4 * kq + i >= lim[rt]) v = -INFINITY;
+          x[4 * h + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));     // the row's four lanes
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__builtin_amdgcn_ballot_w64(mx > m[rt] + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m[rt], mx);
+        const float f = (m_new == m[rt]) ? 1.0f : exp2_fast(m[rt] - m_new);
+        m[rt] = m_new;
+        ell[rt] *= f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[rt][nb] *= f;
+      }
+      float pe[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pe[i] = (x[i] == -INFINITY) ? 0.0f : exp2_fast(x[i] - m[rt]);
+        ell[rt] += pe[i];
+      }
+      pb[rt].x = pack2<BF16>(pe[0], pe[1]);
+      pb[rt].y = pack2<BF16>(pe[2], pe[3]);
+      pb[rt].z = pack2<BF16>(pe[4], pe[5]);
+      pb[rt].w = pack2<BF16>(pe[6], pe[7]);
+      if constexpr (BF16) {
+        // what the rounding left out: p - bf16(p), itself rounded to bf16
+        const uint32_t w[4] = {pb[rt].x, pb[rt].y, pb[rt].z, pb[rt].w};
+        uint32_t r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r[i] = pack2<true>(pe[2 * i] - __builtin_bit_cast(float, w[i] << 16),
+                             pe[2 * i + 1] - __builtin_bit_cast(float, w[i] & 0xffff0000u));
+        pl[rt] = make_uint4(r[0], r[1], r[2], r[3]);
+      }
     }
-    uint2 pb, pl = make_uint2(0, 0);
-    pb.x = pack2<BF16>(pe[0], pe[1]);
-    pb.y = pack2<BF16>(pe[2], pe[3]);
-    if constexpr (BF16) {
-      // what the rounding left out: p - bf16(p), itself rounded to bf16
-      pl.x = pack2<true>(pe[0] - __builtin_bit_cast(float, pb.x << 16), pe[1] - __builtin_bit_cast(float, pb.x & 0xffff0000u));
-      pl.y = pack2<true>(pe[2] - __builtin_bit_cast(float, pb.y << 16), pe[3] - __builtin_bit_cast(float, pb.y & 0xffff0000u));
-    }
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[b]);
+    // P.V: V^T operand of dims 16 nb + row, tokens 4 kq .. +3 and 16 + 4 kq .. +3
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       const int col = 16 * nb + row;
-      uint2 va;
-      va.x = (uint32_t)vt[((0 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((1 * 4 + kq) * kVRow) / 2 + col] << 16);
-      va.y = (uint32_t)vt[((2 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((3 * 4 + kq) * kVRow) / 2 + col] << 16);
-      acc[nb] = mfma_k16<BF16>(va, pb, acc[nb]);
-      if constexpr (BF16) acc[nb] = mfma_k16<BF16>(va, pl, acc[nb]);
-    }
-    // step k+2's tiles into the buffer step k-1 left (every wave finished
-    // with it before the last barrier); the barrier below publishes them and
-    // closes this step's reads of buffer b before step k+3 overwrites it
-    if (k + 2 < nsteps) {
-      store_step(b2, Kn, Vn);
-      if (k + 3 < nsteps) load_step(k + 3, Kn, Vn);
-    }
-    __syncthreads();
-    st = st_next;
-    b = b1;
-  }
-
-  // ---- this wave's 16 rows: sum the four quarters, then store ---------------
-  ell += __shfl_xor(ell, 16);
-  ell += __shfl_xor(ell, 32);
-  const bool live = tq < nq;
-  if (nparts == 1) {
-    if (live) {
-      const float inv = ell > 0.0f ? 1.0f / ell : 0.0f;
-      uint16_t* orow = a.out + ((size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + wrow % GQ) * kD;
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[bb]);
+      uint32_t w[4];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        uint2 w;
-        w.x = pack2<BF16>(acc[nb][0] * inv, acc[nb][1] * inv);
-        w.y = pack2<BF16>(acc[nb][2] * inv, acc[nb][3] * inv);
-        *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * kq) = w;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int t0 = 16 * h + 4 * kq + 2 * i;
+          w[2 * h + i] = (uint32_t)vt[(t0 * kWideRow) / 2 + col] | ((uint32_t)vt[((t0 + 1) * kWideRow) / 2 + col] << 16);
+        }
+      const uint4 va = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        acc[rt][nb] = mfma_k32<BF16>(va, pb[rt], acc[rt][nb]);
+        if constexpr (BF16) acc[rt][nb] = mfma_k32<BF16>(va, pl[rt], acc[rt][nb]);
       }
     }
-    return;
+    // step k+3 into the buffer step k-1 left (every wave finished with it
+    // before the last barrier); the barrier below publishes it and closes
+    // this step's reads of buffer bb before step k+4 overwrites it
+    store_step(k + kWideBufs - 1, Kn, Vn);
+    load_step(k + kWideBufs, Kn, Vn);
+    __syncthreads();
+    if (k + 1 < nsteps) scores((k + 1) % kWideBufs, sc);
   }
-  const size_t pbase = (((size_t)s * a.ntiles + tile) * a.Hkv + kvh) * (size_t)a.nparts_max;
-  float* dst = a.ws_acc + ((pbase + p) * R + wrow) * kD;
+
+  // each row: normaliser over its four lanes, then store
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
-    *reinterpret_cast<float4*>(dst + 16 * nb + 4 * kq) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
-  if (kq == 0) *reinterpret_cast<float2*>(a.ws_ml + ((pbase + p) * R + wrow) * 2) = make_float2(m, ell);
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = ell[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lim[rt] == 0) continue;                  // a padding row: no query
+    const int wrow = (wave * RT + rt) * 16 + row;
+    const int tq = tile * QT + wrow / GQ;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t* orow = a.out + ((size_t)(q0 + tq) * a.Hq + (size_t)kvh * GQ + wrow % GQ) * kD;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      uint2 w;
+      w.x = pack2<BF16>(acc[rt][nb][0] * inv, acc[rt][nb][1] * inv);
+      w.y = pack2<BF16>(acc[rt][nb][2] * inv, acc[rt][nb][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * kq) = w;
+    }
+  }
 }
 
 __global__ void zero_kernel(uint4* p, uint64_t n16, uint8_t* tail, uint64_t ntail) {
@@ -1608,9 +1677,16 @@ bool dispatch_g(int G, bool multi, const DecodeArgs& args, dim3 grid, hipStream_
 // kernel with a query tile); up to 32 on the matrix cores with 16 rows per
 // workgroup, its waves splitting the context; more on the matrix cores with
 // 64 rows per workgroup, its waves splitting the rows over shared LDS tiles.
+// 16-row tiles per wave of the wide kernel at most: two keep two waves per
+// SIMD (four row tiles need one wave per SIMD, and at 64 queries per sequence
+// with four query heads per key/value head took 472-504 us per call against
+// 397-409 us for two)
+constexpr int kWideMaxRt = 2;
+
 struct MqPlan {
   bool mfma = false, wide = false;
   int rows = 8, qt = 1, ntiles = 1;
+  int rt = 1;   // wide: 16-row tiles per wave (rows = 64 rt)
 };
 
 MqPlan mq_plan(int G, int max_q) {
@@ -1618,20 +1694,49 @@ MqPlan mq_plan(int G, int max_q) {
   const int64_t need = (int64_t)max_q * G;
   p.mfma = need > 8;
   p.wide = need > 32;
-  p.rows = p.wide ? 16 * kWaves : (p.mfma ? 16 : 8);
+  if (p.wide) p.rt = need > kWideMaxRt * 32 ? kWideMaxRt : (need > 64 ? 2 : 1);
+  p.rows = p.wide ? 16 * kWaves * p.rt : (p.mfma ? 16 : 8);
   p.qt = p.rows / G;
   p.ntiles = (int)((max_q + p.qt - 1) / p.qt);
   return p;
 }
 
-constexpr int kWidePartMax = 16 * 64;   // a lane holds the block of one 16-token step
+// Sequences longest first (unit = sequence index) for the wide kernel, which
+// walks each sequence's whole context in one workgroup: the longest start
+// first, the shortest fill in at the end.  Returns the count, or -1 when S
+// exceeds one list.
+int order_sequences(const int32_t* host_lens, int S, int max_ctx, UnitList<true>& ul) {
+  if (S > kMaxUnits) return -1;
+  struct U { int len, s; };
+  static thread_local U units[kMaxUnits];
+  for (int s = 0; s < S; ++s) units[s] = {std::min(std::max(host_lens[s], 0), max_ctx), s};
+  std::sort(units, units + S, [](const U& x, const U& y) { return x.len != y.len ? x.len > y.len : x.s < y.s; });
+  for (int c = 0; c < S; ++c) ul.unit[c] = (uint32_t)units[c].s;
+  ul.count = S;
+  return S;
+}
 
-template <bool BF16, int GQ, int BS>
-void launch_mq_rows(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mq_mfma_rows_kernel<BF16, GQ, BS, kWaves>), grid, dim3(kWaves * 64), 0, stream, args);
-  if (args.nparts_max > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, 16 * kWaves, 16 * kWaves / GQ>), dim3(args.Hkv, args.S, args.ntiles),
-                       dim3(16 * kWaves * 16), 0, stream, args);
+template <bool BF16, int GQ, int BS, int RT, bool SCHED>
+void launch_mq_wide(const DecodeArgs& args, const UnitList<SCHED>& ul, hipStream_t stream) {
+  const dim3 grid((unsigned)((uint64_t)args.S * args.ntiles * args.Hkv));
+  hipLaunchKernelGGL((mq_wide_kernel<BF16, GQ, BS, RT, SCHED>), grid, dim3(256), 0, stream, args, ul);
+}
+
+template <bool BF16, int BS, bool SCHED>
+bool dispatch_mq_wide(int G, int rt, const DecodeArgs& args, const UnitList<SCHED>& ul, hipStream_t stream) {
+#define PA_WIDE_CASE(GG)                                                   \
+  case GG:                                                                 \
+    if (rt == 1) launch_mq_wide<BF16, GG, BS, 1, SCHED>(args, ul, stream); \
+    else launch_mq_wide<BF16, GG, BS, 2, SCHED>(args, ul, stream);         \
+    return true;
+  switch (G) {
+    PA_WIDE_CASE(1)
+    PA_WIDE_CASE(2)
+    PA_WIDE_CASE(4)
+    PA_WIDE_CASE(8)
+    default: return false;
+  }
+#undef PA_WIDE_CASE
 }
 
 template <bool BF16, int GQ, int BS>
@@ -1664,16 +1769,7 @@ void launch_mq_mfma(const DecodeArgs& args, dim3 grid, hipStream_t stream) {
 }
 
 template <bool BF16, int BS>
-bool dispatch_mfma(int G, bool wide, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
-  if (wide) {
-    switch (G) {
-      case 1: launch_mq_rows<BF16, 1, BS>(args, grid, stream); return true;
-      case 2: launch_mq_rows<BF16, 2, BS>(args, grid, stream); return true;
-      case 4: launch_mq_rows<BF16, 4, BS>(args, grid, stream); return true;
-      case 8: launch_mq_rows<BF16, 8, BS>(args, grid, stream); return true;
-      default: return false;
-    }
-  }
+bool dispatch_mfma(int G, const DecodeArgs& args, dim3 grid, hipStream_t stream) {
   switch (G) {
     case 1: launch_mq_mfma<BF16, 1, BS>(args, grid, stream); return true;
     case 2: launch_mq_mfma<BF16, 2, BS>(args, grid, stream); return true;
@@ -1733,9 +1829,13 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   LaunchCfg cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, want_list);
   const bool use_list = want_list && order_units(host_lens, S, max_ctx, cfg.part_tokens, ul) > 0;
   if (want_list && !use_list) cfg = choose_launch(S * ntiles, pool->Hkv, max_ctx, false);
-  if (multi && plan.wide && cfg.part_tokens > kWidePartMax) {
-    cfg.part_tokens = kWidePartMax;
-    cfg.nparts_max = max_ctx > 0 ? (max_ctx + cfg.part_tokens - 1) / cfg.part_tokens : 1;
+  // The wide kernel walks a sequence's whole context in one workgroup: no
+  // partitions, no workspace; with host lengths the sequences go longest first.
+  bool wide_list = false;
+  if (multi && plan.wide) {
+    cfg.part_tokens = max_ctx > 0 ? max_ctx : 1;
+    cfg.nparts_max = 1;
+    wide_list = host_lens != nullptr && order_sequences(host_lens, S, max_ctx, ul) > 0;
   }
   const WsLayout wl = ws_layout(S * ntiles, pool->Hkv, rows, cfg);
   char* ws = static_cast<char*>(workspace);
@@ -1780,6 +1880,28 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   const dim3 grid((unsigned)nwg);
   bool ok;
   const bool bf16 = pool->dtype == PA_BF16;
+  if (multi && plan.wide) {      // many rows per sequence: one workgroup walks the whole context
+#define PA_WIDE_B(BB)                                                                          \
+  case BB:                                                                                     \
+    if (wide_list)                                                                             \
+      ok = bf16 ? dispatch_mq_wide<true, BB, true>(G, plan.rt, args, ul, stream)               \
+                : dispatch_mq_wide<false, BB, true>(G, plan.rt, args, ul, stream);             \
+    else                                                                                       \
+      ok = bf16 ? dispatch_mq_wide<true, BB, false>(G, plan.rt, args, UnitList<false>{}, stream) \
+                : dispatch_mq_wide<false, BB, false>(G, plan.rt, args, UnitList<false>{}, stream); \
+    break;
+    switch (pool->B) {
+      PA_WIDE_B(8)
+      PA_WIDE_B(16)
+      PA_WIDE_B(32)
+      PA_WIDE_B(64)
+      default:
+      PA_WIDE_B(128)
+    }
+#undef PA_WIDE_B
+    if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+    return hip_check(hipGetLastError(), "multi-query attention launch");
+  }
   if (use_list && multi) {       // several queries per sequence, one tile each
     switch (pool->B) {
       case 8: ok = bf16 ? dispatch_mq_ordered<true, 8>(G, args, ul, stream) : dispatch_mq_ordered<false, 8>(G, args, ul, stream); break;
@@ -1804,11 +1926,11 @@ pa_status decode_launch(pa_pool* pool, int layer, void* out, const void* q, int 
   }
   if (multi && plan.mfma) {
     switch (pool->B) {
-      case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 8>(G, plan.wide, args, grid, stream); break;
-      case 16: ok = bf16 ? dispatch_mfma<true, 16>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 16>(G, plan.wide, args, grid, stream); break;
-      case 32: ok = bf16 ? dispatch_mfma<true, 32>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 32>(G, plan.wide, args, grid, stream); break;
-      case 64: ok = bf16 ? dispatch_mfma<true, 64>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 64>(G, plan.wide, args, grid, stream); break;
-      default: ok = bf16 ? dispatch_mfma<true, 128>(G, plan.wide, args, grid, stream) : dispatch_mfma<false, 128>(G, plan.wide, args, grid, stream); break;
+      case 8: ok = bf16 ? dispatch_mfma<true, 8>(G, args, grid, stream) : dispatch_mfma<false, 8>(G, args, grid, stream); break;
+      case 16: ok = bf16 ? dispatch_mfma<true, 16>(G, args, grid, stream) : dispatch_mfma<false, 16>(G, args, grid, stream); break;
+      case 32: ok = bf16 ? dispatch_mfma<true, 32>(G, args, grid, stream) : dispatch_mfma<false, 32>(G, args, grid, stream); break;
+      case 64: ok = bf16 ? dispatch_mfma<true, 64>(G, args, grid, stream) : dispatch_mfma<false, 64>(G, args, grid, stream); break;
+      default: ok = bf16 ? dispatch_mfma<true, 128>(G, args, grid, stream) : dispatch_mfma<false, 128>(G, args, grid, stream); break;
     }
     if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
     return hip_check(hipGetLastError(), "multi-query attention launch");

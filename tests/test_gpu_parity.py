@@ -750,6 +750,54 @@ def test_multi_query_shapes_ragged(G, Hkv, B, dtype):
     _say(f"worst max_abs {worst:.2e}")
 
 
+@pytest.mark.parametrize("G,Hkv,B,dtype,max_q", [
+    (4, 2, 16, "bf16", 64),      # 256 rows per sequence: four 16-row tiles per wave
+    (4, 2, 8, "f16", 100),       # more rows than one workgroup holds: two row tiles
+    (1, 3, 32, "bf16", 100),     # two 16-row tiles per wave
+    (2, 2, 16, "f16", 20),       # one tile per wave
+    (8, 1, 64, "bf16", 40),      # two workgroup row tiles of 32 query tokens
+])
+def test_multi_query_wide_path_both_orders(G, Hkv, B, dtype, max_q):
+    """More than 32 rows per sequence: one workgroup walks a sequence's whole
+    context for up to 256 rows.  Launched in the fixed order and longest
+    first (host lengths); both equal the oracle within tolerance and each
+    other bit for bit.  Ragged query counts up to whole prefills (nq = n),
+    contexts from 1 to 3,000 positions."""
+    from oracle.decode import multi_query_one
+    from paged_kv_cache_239_amd import multi_query_workspace
+    _say(f"multi-query wide G={G} Hkv={Hkv} B={B} {dtype} max_q={max_q}")
+    rng = np.random.default_rng(7000 + 31 * G + B + max_q)
+    lens = [max_q, 3000, 45, max_q + 1, 777, 2049, 130, 1, 64, 1500]
+    nqs = [min(x, max_q) for x in (max_q, max_q, 45, max_q, 33, max_q - 1, 17, 1, 64, max_q)]
+    S = len(lens)
+    Hq = G * Hkv
+    pool, host, tables, _ = _direct_case(rng, S, Hq, Hkv, B, dtype, lens)
+    T = int(sum(nqs))
+    q = round_to_dtype_bits(rng.standard_normal((T, Hq, 128)).astype(np.float32), dtype)
+    q_start = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    ws = multi_query_workspace(pool, S, Hq, max(lens), max_q)
+    dq = to_device_bits(q, dtype)
+    outs = []
+    for ordered in (False, True):
+        out = torch.full_like(dq, float("nan"))
+        pool.multi_query_attention(0, out, dq, torch.from_numpy(q_start).cuda(), torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(), max(lens), max_q, scale,
+                                   workspace=ws, host_context_lens=np.asarray(lens, dtype=np.int32) if ordered else None)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = to_host_f64(outs[1], dtype)
+    worst = 0.0
+    for s in range(S):
+        rows = slice(q_start[s], q_start[s + 1])
+        ref = multi_query_one(host, 0, q[rows], tables[s], lens[s], scale, dtype)
+        ok, st = within_tolerance(got[rows], ref, dtype)
+        assert ok, (s, lens[s], nqs[s], st)
+        worst = max(worst, st["max_abs"])
+    _say(f"worst max_abs {worst:.2e}")
+
+
 def test_multi_query_one_query_each_matches_decode_within_tolerance():
     """nq = 1 everywhere: the multi-query path agrees with the oracle's decode
     (and so with pa_decode_attention) on the same inputs."""
@@ -1021,10 +1069,12 @@ def test_config4_every_layer_every_sequence(oracle_pool):
 
 def test_config5_fork_step_cow_sources_unchanged_debug_engine():
     """The fork step of the parallel-sampling workload with the engine in
-    debug mode (pa_validate_step on every step): after the copies and the
-    fused writes, every copy-on-write source block is bitwise unchanged in
-    every layer, and every copy equals its source except the one row per
-    (layer, key or value, head) that the step writes -- the new token's."""
+    debug mode (pa_validate_step on every step).  Three of a prompt's four
+    branches copy its partial last block; the fourth then finds the count at
+    one and writes in place.  After the copies and the fused writes, in every
+    layer: every copy equals its source except the one row per (key or
+    value, head) that its own branch writes, and every source block differs
+    from its former contents only in the row written in place, if any."""
     _say("config 5 fork step, debug engine, copy-on-write sources")
     wl = with_headroom(make_workload(5), 1)
     c = wl.cfg
@@ -1039,21 +1089,30 @@ def test_config5_fork_step_cow_sources_unchanged_debug_engine():
     assert len(pairs) > 100
     tile = eng.pool.nbytes // (2 * c.L * wl.P)
     view = eng.pool.buffer.view(2 * c.L, wl.P, tile)
-    src_idx = torch.from_numpy(pairs[:, 0].astype(np.int64)).cuda()
+    srcs = sorted(set(pairs[:, 0].tolist()))
+    src_idx = torch.tensor(srcs, dtype=torch.int64, device="cuda")
     dst_idx = torch.from_numpy(pairs[:, 1].astype(np.int64)).cuda()
     before = view.index_select(1, src_idx).clone()
     eng.device_step(qs, ks, vs, outs, max_ctx, float(wl.scale))
     torch.cuda.synchronize()
-    assert torch.equal(view.index_select(1, src_idx), before)
-    # the copies: equal to the source but for the written row of each head
+    written = {}                                  # block -> rows the step writes into it
+    for slot in eng.last_slots.tolist():
+        written.setdefault(int(slot) // c.B, []).append(int(slot) % c.B)
     row = c.d * 2
-    dst = view.index_select(1, dst_idx).view(2 * c.L, len(pairs), c.Hkv, c.B, row)
-    src = before.view(2 * c.L, len(pairs), c.Hkv, c.B, row)
-    slot_of = {}
-    for s, slot in enumerate(eng.last_slots.tolist()):
-        slot_of[int(slot) // c.B] = int(slot) % c.B
-    diff = (dst != src).any(dim=-1).any(dim=0).any(dim=1).cpu().numpy()      # [pairs][B]: rows that changed
+
+    def changed_rows(a, b):                       # [2L][n][tile] pair -> per block, rows that differ anywhere
+        d = (a.view(2 * c.L, a.shape[1], c.Hkv, c.B, row) != b.view(2 * c.L, b.shape[1], c.Hkv, c.B, row))
+        return d.any(dim=-1).any(dim=0).any(dim=1).cpu().numpy()      # [n][B]
+
+    after_src = view.index_select(1, src_idx)
+    diff = changed_rows(after_src, before)
+    for i, b in enumerate(srcs):
+        assert np.nonzero(diff[i])[0].tolist() == sorted(written.get(b, [])), b
+    pos = {b: i for i, b in enumerate(srcs)}
+    dst = view.index_select(1, dst_idx)
+    src_before = before.index_select(1, torch.tensor([pos[a] for a in pairs[:, 0].tolist()], device="cuda"))
+    diff = changed_rows(dst, src_before)
     for i, (a, b) in enumerate(pairs.tolist()):
-        changed = np.nonzero(diff[i])[0].tolist()
-        assert changed == [slot_of[b]], (a, b, changed)
-    _say(f"{len(pairs)} copies checked over {c.L} layers")
+        assert np.nonzero(diff[i])[0].tolist() == sorted(written[b]), (a, b)
+    in_place = sum(1 for b in srcs if b in written)
+    _say(f"{len(pairs)} copies of {len(srcs)} blocks checked over {c.L} layers; {in_place} sources written in place")
