@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 # the attention kernel's sources: a counter record applies only to these exact files
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_239_amd", "csrc", f)
                   for f in ("pa_attention.hip", "pa_device_common.h")]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_attention_gqa32x8_bf16_b16_pmc.md")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_sha() -> str:
@@ -48,19 +48,22 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary, or None if that summary was taken on another
-    version of the kernel source."""
-    try:
-        text = open(PMC_SUMMARY).read()
-        block = text.split("```json", 1)[1].split("```", 1)[0]
-        rec = json.loads(block)
-    except (OSError, IndexError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256") != kernel_source_sha():
-        return None
-    return rec
+def recorded_traffic(here: dict):
+    """HBM bytes per attention call from a committed rocprofv3 counter
+    summary (profiles/*_pmc.md, a JSON record each) taken on this workload
+    and launch mode (``here``) and on this version of the kernel source, or
+    None when there is none."""
+    import glob
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_pmc.md"))):
+        try:
+            text = open(path).read()
+            rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        except (OSError, IndexError, ValueError):
+            continue
+        if rec.get("kernel_source_sha256") == sha and rec.get("workload") == here:
+            return rec
+    return None
 
 
 class HipEvents:
@@ -441,11 +444,11 @@ def run(args, opool) -> int:
         result["roofline"]["note"] = ("achieved and value count a block that several sequences map once "
                                       "(unique bytes); the logical figures count it once per sequence, "
                                       "and may exceed the HBM peak since repeated reads hit in cache")
-    rec = recorded_traffic()
     # counters apply only to the workload and launch mode they were taken on
     here = {"config": args.config, "block_size": c.B, "head_shards": args.head_shards or 1,
             "order": args.order, "grouped": bool(grouped)}
-    if rec is not None and rec.get("workload") == here:
+    rec = recorded_traffic(here)
+    if rec is not None:
         result["roofline"]["traffic"] = int(rec["traffic_bytes_per_launch"])
         result["roofline"]["traffic_note"] = (
             f"rocprofv3 FETCH_SIZE x{rec['fetch_scale']} + WRITE_SIZE x{rec['write_scale']} per launch "
@@ -600,8 +603,15 @@ def multi_query_bench(args) -> int:
                      "avg_launch_us": round(att_us, 2),
                      "note": "bound from the arithmetic intensity of the algorithmic bytes and flops against "
                              "the ridge point; compute peak: dense 16-bit MFMA 2.5 PFLOP/s on the matrix path, "
-                             "fp32 vector 157.3 TFLOP/s on the vector path"},
+                             "fp32 vector 157.3 TFLOP/s on the vector path",
+                     "traffic": None},
     }
+    rec = recorded_traffic({"config": args.config, "block_size": c.B, "queries": Q, "order": args.order})
+    if rec is not None:
+        res["roofline"]["traffic"] = int(rec["traffic_bytes_per_launch"])
+        res["roofline"]["traffic_note"] = (
+            f"rocprofv3 FETCH_SIZE x{rec['fetch_scale']} + WRITE_SIZE x{rec['write_scale']} per call, at "
+            f"{rec['alg_bytes_per_launch']} algorithmic bytes; traffic / algorithmic = {rec['traffic_over_alg']}")
     print(json.dumps(res), flush=True)
     return 0
 

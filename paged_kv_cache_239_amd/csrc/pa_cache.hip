@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(const char* f
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 8;       // 16-byte loads per thread per tile issued together
 constexpr int kStreamMaxSeqs = 2048;   // 16 KiB of LDS for the prefix and lengths
-constexpr int kStreamWgPerCu = 4;
+constexpr int kStreamWgPerCu = 1;      // config-3 batch: 94 us per layer at 1, 97-100 at 2, 105-111 at 4
 
 struct StreamArgs {
   const char* kslab;
@@ -165,15 +165,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_tiles_kernel(const Stre
     const int mid = (lo + hi + 1) >> 1;
     if (s_pre[mid] <= i0) lo = mid; else hi = mid - 1;
   }
-  int s = lo;
+  // the walk is uniform: keep it in scalar registers, so that each block's
+  // table entry is a scalar (constant-cache) load rather than a vector
+  // memory round trip before the block's data loads
+  int s = __builtin_amdgcn_readfirstlane(lo);
   const int nch = (int)(a.tile_bytes / 16);   // 16-byte chunks per tile; chunk k is row (k / 16) % BS
   uint32_t x = 0;
   for (int i = i0; i < i1; ++i) {
-    while (s_pre[s + 1] <= i) ++s;
-    const int j = i - s_pre[s];
-    const int rows = min(BS, s_len[s] - j * BS);
+    while (__builtin_amdgcn_readfirstlane(s_pre[s + 1]) <= i) ++s;
+    const int j = i - __builtin_amdgcn_readfirstlane(s_pre[s]);
+    const int rows = min(BS, __builtin_amdgcn_readfirstlane(s_len[s]) - j * BS);
     int e = a.tables[(size_t)s * a.maxb + (j < a.maxb ? j : a.maxb - 1)];
-    e = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
+    e = __builtin_amdgcn_readfirstlane(e < 0 ? 0 : (e >= a.P ? a.P - 1 : e));
     const char* kb = a.kslab + (uint64_t)e * a.tile_bytes;
     const char* vb = a.vslab + (uint64_t)e * a.tile_bytes;
     for (int k0 = t; k0 < nch; k0 += kStreamThreads * kStreamUnroll) {
