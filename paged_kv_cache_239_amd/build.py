@@ -26,9 +26,13 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU instructions are kept out of every kernel.
+# Packed-fp32 VALU instructions are kept out of every kernel.  Matrix-core
+# accumulators stay in ordinary vector registers: left to the compiler's
+# heuristic they move between the accumulation and the vector file on every
+# step of the attention loops (the online-softmax rescale reads them).
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
 
 

@@ -60,6 +60,7 @@
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "pa_device_common.h"
@@ -1239,10 +1240,17 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 // partial results to merge; further row tiles of the same sequence and head
 // are further workgroups, dealt to the same XCD (head fastest in the grid),
 // whose reads of the context mostly hit its L2.  Four waves own RT 16-row
-// tiles each (wave w: rows 16 RT w ..);
-// all waves share the 32-token steps, staged by the workgroup in a ring of
-// four LDS buffers (three steps in flight, one barrier per step).  Per step
-// and row tile, on the matrix cores (16x16x32 for both products):
+// tiles each (wave w: rows 16 RT w ..); all waves share the 32-token steps.
+// Keys and values travel from HBM straight into a ring of four LDS slots
+// (direct-to-LDS loads, no registers in between), so three steps are in
+// flight while one is computed; one barrier per step both publishes the
+// step that landed and frees the slot the step before used.  A load
+// instruction fills 1 KB of LDS (four token rows), lane by lane.  Key rows:
+// token t's 16-byte chunk c sits at position c ^ (t % 16), so the 16 tokens
+// whose rows one MFMA operand reads spread over all banks.  Value rows stay
+// in order, each group of four rows 32 bytes past the last, so the columns
+// one operand gathers from four such groups fall in distinct banks.  Per
+// step and row tile, on the matrix cores (16x16x32 for both products):
 //   S^T[token][row] = K[token][:] . Q[row][:] for the step's two 16-token
 //       halves h: A = K rows of half h (lane: token lane % 16, dims
 //       32 ks + 8 kq .. +7, read from LDS), B = Q^T held in registers; lane
@@ -1250,15 +1258,24 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 //   O^T[dim][row] += V^T[dim][token] . P^T[token][row] with the step's 32
 //       tokens ordered so that lane (row, kq) supplies exactly its own eight
 //       probabilities (tokens 4 kq .. +3 and 16 + 4 kq .. +3) as B; A = V^T in
-//       the same token order, gathered from the row-major LDS value tile;
+//       the same token order, gathered from the LDS value rows;
 //       lane (row, kq) accumulates dims 16 nb + 4 kq .. +3 of its row.
 // The row's running maximum and normaliser live in the four lanes of the
 // row (one per kq); bf16 probabilities enter P.V as a rounded part plus the
 // rounded remainder (two products), fp16 ones as one.
 constexpr int kWideTok = 32;                    // tokens per step
-constexpr int kWideBufs = 4;                    // LDS ring: steps k .. k+3
-constexpr int kWideRow = 272;                   // LDS bytes per token row (256 + 16 pad)
+constexpr int kWideBufs = 4;                    // LDS ring slots: step k and the three after it
 constexpr int kWideTabMax = 2048;               // table entries cached in LDS
+constexpr int kWideVGroup = 66;                 // 16-byte chunks per group of four value rows (+2 pad)
+constexpr int kWideSlot = kWideTok * 16 + (kWideTok / 4) * kWideVGroup;   // chunks per slot: keys, then values
+// direct-to-LDS loads per lane and step: two key and two value chunks
+constexpr int kWideLoadsPerStep = 4;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate (gfx9 layout): vector-memory count vm, LDS count lgkm,
+// export count left at its maximum
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (lgkm << 8); }
 
 
 template <bool BF16, int GQ, int BS, int RT, bool SCHED>
@@ -1325,15 +1342,16 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
     wave_lim_min = __builtin_amdgcn_readfirstlane(v);
   }
 
-  // LDS ring of step tiles, keys and values both row-major [token][dim]
-  __shared__ __attribute__((aligned(16))) char s_k[kWideBufs][kWideTok * kWideRow];
-  __shared__ __attribute__((aligned(16))) char s_v[kWideBufs][kWideTok * kWideRow];
+  // The ring slots are separate objects: the compiler then sees that a read
+  // of one slot does not depend on the loads still landing in the others,
+  // and leaves their waits to the explicit counts below.
+  __shared__ __attribute__((aligned(16))) uint4 ring0[kWideSlot];
+  __shared__ __attribute__((aligned(16))) uint4 ring1[kWideSlot];
+  __shared__ __attribute__((aligned(16))) uint4 ring2[kWideSlot];
+  __shared__ __attribute__((aligned(16))) uint4 ring3[kWideSlot];
   // the sequence's table row (physical blocks, clamped into the pool)
   __shared__ int s_tab[kWideTabMax];
 
-  // this thread's share of a step: tokens lt and lt + 16, 16 bytes at dims 8 lc
-  const int lt = tid >> 4;
-  const int lc = tid & 15;
   const uint64_t head_off = (uint64_t)kvh * BS * kRowBytes;
   const int32_t* table = a.tables + (size_t)s * a.maxb;
   const int nblk = (n_wg + BS - 1) / BS;
@@ -1345,14 +1363,20 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
     }
   }
   __syncthreads();
-  // Every iteration issues the same four 16-byte loads (the step index and
-  // the position are clamped, rows past n_wg are zeroed when stored), so the
-  // compiler's wait before a store covers exactly the oldest stage.
-  auto load_step = [&](int k, uint4 (&Kx)[2], uint4 (&Vx)[2]) {
+
+  // Step k into a slot: each wave fills token rows 8 wave .. +7, one load
+  // instruction per four rows and tensor; lane l lands in position l % 16 of
+  // row l / 16, so it fetches the chunk that belongs there.  Every call
+  // issues the same four loads (the step and the position are clamped; rows
+  // past n_wg repeat a position the workgroup reads, and no row sees them),
+  // so the wait counts below are exact.
+  const int my_t = 8 * wave + (lane >> 4);
+  auto issue = [&](int k, uint4* slot) {
     const int kc = min(k, nsteps - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int tok = min(kc * kWideTok + lt + 16 * j, n_wg - 1);
+      const int t = my_t + 4 * j;
+      const int tok = min(kc * kWideTok + t, n_wg - 1);
       int phys;
       if (tab_lds) {
         phys = s_tab[tok / BS];
@@ -1360,21 +1384,12 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         const int e = table[tok / BS];
         phys = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
       }
-      const uint64_t off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes + lc * 16;
-      Kx[j] = nt_load16(a.kslab + off);
-      Vx[j] = nt_load16(a.vslab + off);
-    }
-  };
-  auto store_step = [&](int k, const uint4 (&Kx)[2], const uint4 (&Vx)[2]) {
-    const int bb = k % kWideBufs;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // component-wise selects: a select of whole vector structs goes through memory
-      const uint32_t keep = k * kWideTok + lt + 16 * j < n_wg ? 0xffffffffu : 0u;
-      const uint4 kx = make_uint4(Kx[j].x & keep, Kx[j].y & keep, Kx[j].z & keep, Kx[j].w & keep);
-      const uint4 vx = make_uint4(Vx[j].x & keep, Vx[j].y & keep, Vx[j].z & keep, Vx[j].w & keep);
-      *reinterpret_cast<uint4*>(s_k[bb] + (lt + 16 * j) * kWideRow + lc * 16) = kx;
-      *reinterpret_cast<uint4*>(s_v[bb] + (lt + 16 * j) * kWideRow + lc * 16) = vx;
+      const uint64_t row_off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes;
+      const int kc16 = ((lane & 15) ^ (t & 15)) * 16;     // key: the swizzled chunk
+      const int vc16 = (lane & 15) * 16;                  // value: rows in order
+      __builtin_amdgcn_global_load_lds(a.kslab + row_off + kc16, (lds_void_t*)(slot + (8 * wave + 4 * j) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.vslab + row_off + vc16,
+                                       (lds_void_t*)(slot + kWideTok * 16 + (2 * wave + j) * kWideVGroup), 16, 0, 0);
     }
   };
 
@@ -1388,24 +1403,28 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
     for (int nb = 0; nb < 8; ++nb) acc[rt][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // prologue: steps 0 .. 2 in LDS, step 3 in registers
-  uint4 Kn[2], Vn[2];
-#pragma unroll
-  for (int k = 0; k < kWideBufs - 1; ++k) {
-    load_step(k, Kn, Vn);
-    store_step(k, Kn, Vn);
-  }
-  load_step(kWideBufs - 1, Kn, Vn);
-  __syncthreads();
+  // One step from its slot; next: the slot of the step before, refilled
+  // with step k + 3.  EDGE: some row of the wave stops inside the step
+  // (per-row masks, and a row may have seen no position yet); otherwise
+  // every score is finite.
+  auto run_step = [&](int k, const uint4* slot, uint4* next, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    // this lane's loads of step k have landed (the three later steps may
+    // still be in flight) and its reads of step k-1 are done; after the
+    // barrier the same holds for every lane
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kWideBufs - 2) * kWideLoadsPerStep, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(k + kWideBufs - 1, next);
+    const int tok0 = k * kWideTok;
 
-  // scores of the step in buffer b: two 16-token halves x RT row tiles
-  auto scores = [&](int b, f32x4_t (&sc)[RT][2]) {
+    // scores: two 16-token halves x RT row tiles
+    f32x4_t sc[RT][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 kx[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kx[ks] = *reinterpret_cast<const uint4*>(s_k[b] + (16 * h + row) * kWideRow + (32 * ks + 8 * kq) * 2);
+      for (int ks = 0; ks < 4; ++ks) kx[ks] = slot[(16 * h + row) * 16 + ((4 * ks + kq) ^ row)];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         f32x4_t st = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1414,17 +1433,7 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         sc[rt][h] = st;
       }
     }
-  };
 
-  // (Issuing step k+1's score products before step k's softmax, a deeper
-  // register prefetch, values staged transposed and four row tiles per wave
-  // at one wave per SIMD were all slower at 64 queries per sequence.)
-  f32x4_t sc[RT][2];
-  scores(0, sc);
-  for (int k = 0; k < nsteps; ++k) {
-    const int bb = k % kWideBufs;
-    const int tok0 = k * kWideTok;
-    const bool edge = tok0 + kWideTok > wave_lim_min;   // some row of the wave stops inside this step
     // online softmax per row tile; probabilities in the storage type
     uint4 pb[RT], pl[RT];
 #pragma unroll
@@ -1436,7 +1445,7 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sc[rt][h][i] * a.scale_log2;
-          if (edge && tok0 + 16 * h + 4 * kq + i >= lim[rt]) v = -INFINITY;
+          if (EDGE && tok0 + 16 * h + 4 * kq + i >= lim[rt]) v = -INFINITY;
           x[4 * h + i] = v;
           mx = fmaxf(mx, v);
         }
@@ -1453,7 +1462,7 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
       float pe[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pe[i] = (x[i] == -INFINITY) ? 0.0f : exp2_fast(x[i] - m[rt]);
+        pe[i] = (EDGE && x[i] == -INFINITY) ? 0.0f : exp2_fast(x[i] - m[rt]);
         ell[rt] += pe[i];
       }
       pb[rt].x = pack2<BF16>(pe[0], pe[1]);
@@ -1471,18 +1480,19 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         pl[rt] = make_uint4(r[0], r[1], r[2], r[3]);
       }
     }
+
     // P.V: V^T operand of dims 16 nb + row, tokens 4 kq .. +3 and 16 + 4 kq .. +3
+    // (token 16 h + 4 kq + r: row r of value group 4 h + kq)
+    const uint16_t* vt = reinterpret_cast<const uint16_t*>(slot + kWideTok * 16) + kq * (kWideVGroup * 8) + row;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const int col = 16 * nb + row;
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[bb]);
       uint32_t w[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int t0 = 16 * h + 4 * kq + 2 * i;
-          w[2 * h + i] = (uint32_t)vt[(t0 * kWideRow) / 2 + col] | ((uint32_t)vt[((t0 + 1) * kWideRow) / 2 + col] << 16);
+          const uint16_t* g = vt + 4 * h * (kWideVGroup * 8) + 16 * nb;
+          w[2 * h + i] = (uint32_t)g[(2 * i) * 128] | ((uint32_t)g[(2 * i + 1) * 128] << 16);
         }
       const uint4 va = make_uint4(w[0], w[1], w[2], w[3]);
 #pragma unroll
@@ -1491,14 +1501,33 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         if constexpr (BF16) acc[rt][nb] = mfma_k32<BF16>(va, pl[rt], acc[rt][nb]);
       }
     }
-    // step k+3 into the buffer step k-1 left (every wave finished with it
-    // before the last barrier); the barrier below publishes it and closes
-    // this step's reads of buffer bb before step k+4 overwrites it
-    store_step(k + kWideBufs - 1, Kn, Vn);
-    load_step(k + kWideBufs, Kn, Vn);
-    __syncthreads();
-    if (k + 1 < nsteps) scores((k + 1) % kWideBufs, sc);
+  };
+
+  // prologue: steps 0 .. 2 in flight
+  issue(0, ring0);
+  issue(1, ring1);
+  issue(2, ring2);
+  // steps every live row of the wave sees whole, four at a time so that each
+  // slot is a fixed object; then the rest with masks
+  const int k_edge = min(nsteps, wave_lim_min / kWideTok);
+  int k = 0;
+  for (; k + 4 <= k_edge; k += 4) {
+    run_step(k, ring0, ring3, std::false_type{});
+    run_step(k + 1, ring1, ring0, std::false_type{});
+    run_step(k + 2, ring2, ring1, std::false_type{});
+    run_step(k + 3, ring3, ring2, std::false_type{});
   }
+  for (; k < nsteps; ++k) {
+    switch (k & 3) {
+      case 0: run_step(k, ring0, ring3, std::true_type{}); break;
+      case 1: run_step(k, ring1, ring0, std::true_type{}); break;
+      case 2: run_step(k, ring2, ring1, std::true_type{}); break;
+      default: run_step(k, ring3, ring2, std::true_type{}); break;
+    }
+  }
+  // the clamped loads issued past the last step land before the workgroup's
+  // LDS is released
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   // each row: normaliser over its four lanes, then store
 #pragma unroll
