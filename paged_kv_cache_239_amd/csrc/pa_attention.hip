@@ -1247,10 +1247,13 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 // step that landed and frees the slot the step before used.  A load
 // instruction fills 1 KB of LDS (four token rows), lane by lane.  Key rows:
 // token t's 16-byte chunk c sits at position c ^ (t % 16), so the 16 tokens
-// whose rows one MFMA operand reads spread over all banks.  Value rows stay
-// in order, each group of four rows 32 bytes past the last, so the columns
-// one operand gathers from four such groups fall in distinct banks.  Per
-// step and row tile, on the matrix cores (16x16x32 for both products):
+// whose rows one MFMA operand reads spread over all banks.  Values: each
+// group of four token rows (one load instruction) 128 bytes past the last,
+// and row e's chunk c at position c ^ 2e, so that the transposing LDS read
+// (ds_read_b64_tr_b16: lane a + 4e of a 16-lane group addresses four
+// elements of row e, lane 4a + b receives element b of rows 0..3) that
+// builds a V^T operand touches distinct banks.  Per step and row tile, on
+// the matrix cores (16x16x32 for both products):
 //   S^T[token][row] = K[token][:] . Q[row][:] for the step's two 16-token
 //       halves h: A = K rows of half h (lane: token lane % 16, dims
 //       32 ks + 8 kq .. +7, read from LDS), B = Q^T held in registers; lane
@@ -1258,7 +1261,7 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 //   O^T[dim][row] += V^T[dim][token] . P^T[token][row] with the step's 32
 //       tokens ordered so that lane (row, kq) supplies exactly its own eight
 //       probabilities (tokens 4 kq .. +3 and 16 + 4 kq .. +3) as B; A = V^T in
-//       the same token order, gathered from the LDS value rows;
+//       the same token order, two transposing reads per operand;
 //       lane (row, kq) accumulates dims 16 nb + 4 kq .. +3 of its row.
 // The row's running maximum and normaliser live in the four lanes of the
 // row (one per kq); bf16 probabilities enter P.V as a rounded part plus the
@@ -1266,12 +1269,14 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 constexpr int kWideTok = 32;                    // tokens per step
 constexpr int kWideBufs = 4;                    // LDS ring slots: step k and the three after it
 constexpr int kWideTabMax = 2048;               // table entries cached in LDS
-constexpr int kWideVGroup = 66;                 // 16-byte chunks per group of four value rows (+2 pad)
+constexpr int kWideVGroup = 72;                 // 16-byte chunks per group of four value rows (+8 pad)
 constexpr int kWideSlot = kWideTok * 16 + (kWideTok / 4) * kWideVGroup;   // chunks per slot: keys, then values
 // direct-to-LDS loads per lane and step: two key and two value chunks
 constexpr int kWideLoadsPerStep = 4;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // s_waitcnt immediate (gfx9 layout): vector-memory count vm, LDS count lgkm,
 // export count left at its maximum
@@ -1279,7 +1284,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 
 
 
 template <bool BF16, int GQ, int BS, int RT, bool SCHED>
-__global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const UnitList<SCHED> ul) {
+__global__ __launch_bounds__(256, 2) void mq_wide_kernel(const DecodeArgs a, const UnitList<SCHED> ul) {
   constexpr int NW = 4;
   constexpr int R = 16 * RT * NW;                 // rows per workgroup
   constexpr int QT = R / GQ;                      // query tokens per workgroup
@@ -1330,6 +1335,20 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[rt][ks] = live ? qrow[4 * ks + kq] : make_uint4(0, 0, 0, 0);
   }
+  // scores enter the exponent as fma(s, c, -m) with c > 0: for a negative
+  // scale the query changes sign instead (exact in 16-bit floats)
+  const float c_log2 = fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.0f) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qb[rt][ks].x ^= 0x80008000u;
+        qb[rt][ks].y ^= 0x80008000u;
+        qb[rt][ks].z ^= 0x80008000u;
+        qb[rt][ks].w ^= 0x80008000u;
+      }
+  }
   // the first position some row of this wave cannot see: steps before it need no mask
   int wave_lim_min;
   {
@@ -1371,8 +1390,38 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
   // past n_wg repeat a position the workgroup reads, and no row sees them),
   // so the wait counts below are exact.
   const int my_t = 8 * wave + (lane >> 4);
+  const int kc16 = (lane & 15) ^ (my_t & 15);          // key: chunk at position ^ (t % 16), t = my_t + 4 j
+  const int kc16b = (lane & 15) ^ ((my_t + 4) & 15);
+  const int vc16 = (lane & 15) ^ (2 * (lane >> 4));    // value: row t % 4 = lane / 16
+  // a whole step's token t: with B < 32 block 32 step / B + t / B, row t % B;
+  // with B >= 32 the step's tokens share block 32 step / B, rows 32 step % B + t
+  int lane_blk[2];
+  uint32_t lane_k[2], lane_v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = my_t + 4 * j;
+    lane_blk[j] = BS < kWideTok ? t / BS : 0;
+    const uint32_t row_b = (uint32_t)head_off + (uint32_t)(BS < kWideTok ? t % BS : t) * kRowBytes;
+    lane_k[j] = row_b + (j ? kc16b : kc16) * 16;
+    lane_v[j] = row_b + vc16 * 16;
+  }
   auto issue = [&](int k, uint4* slot) {
     const int kc = min(k, nsteps - 1);
+    if (tab_lds && kc * kWideTok + kWideTok <= n_wg) {
+      const int blk0 = kc * kWideTok / BS;
+      const uint32_t step_row = BS < kWideTok ? 0u : (uint32_t)(kc * kWideTok % BS) * kRowBytes;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint64_t base = (uint64_t)s_tab[blk0 + lane_blk[j]] * a.tile_bytes + step_row;
+        __builtin_amdgcn_global_load_lds(a.kslab + base + lane_k[j], (lds_void_t*)(slot + (8 * wave + 4 * j) * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.vslab + base + lane_v[j],
+                                         (lds_void_t*)(slot + kWideTok * 16 + (2 * wave + j) * kWideVGroup), 16, 0, 0);
+      }
+      return;
+    }
+    // the last step (positions clamped to n_wg - 1: rows past it repeat a
+    // position the workgroup reads, and no row sees them), or a table too
+    // long for LDS
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = my_t + 4 * j;
@@ -1385,10 +1434,9 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         phys = e < 0 ? 0 : (e >= a.P ? a.P - 1 : e);
       }
       const uint64_t row_off = (uint64_t)phys * a.tile_bytes + head_off + (uint64_t)(tok % BS) * kRowBytes;
-      const int kc16 = ((lane & 15) ^ (t & 15)) * 16;     // key: the swizzled chunk
-      const int vc16 = (lane & 15) * 16;                  // value: rows in order
-      __builtin_amdgcn_global_load_lds(a.kslab + row_off + kc16, (lds_void_t*)(slot + (8 * wave + 4 * j) * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.vslab + row_off + vc16,
+      __builtin_amdgcn_global_load_lds(a.kslab + row_off + (j ? kc16b : kc16) * 16,
+                                       (lds_void_t*)(slot + (8 * wave + 4 * j) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.vslab + row_off + vc16 * 16,
                                        (lds_void_t*)(slot + kWideTok * 16 + (2 * wave + j) * kWideVGroup), 16, 0, 0);
     }
   };
@@ -1403,23 +1451,8 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
     for (int nb = 0; nb < 8; ++nb) acc[rt][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // One step from its slot; next: the slot of the step before, refilled
-  // with step k + 3.  EDGE: some row of the wave stops inside the step
-  // (per-row masks, and a row may have seen no position yet); otherwise
-  // every score is finite.
-  auto run_step = [&](int k, const uint4* slot, uint4* next, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    // this lane's loads of step k have landed (the three later steps may
-    // still be in flight) and its reads of step k-1 are done; after the
-    // barrier the same holds for every lane
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kWideBufs - 2) * kWideLoadsPerStep, 0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(k + kWideBufs - 1, next);
-    const int tok0 = k * kWideTok;
-
-    // scores: two 16-token halves x RT row tiles
-    f32x4_t sc[RT][2];
+  // scores of a step: two 16-token halves x RT row tiles
+  auto scores = [&](const uint4* slot, f32x4_t (&sc)[RT][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 kx[4];
@@ -1433,24 +1466,49 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         sc[rt][h] = st;
       }
     }
+  };
 
-    // online softmax per row tile; probabilities in the storage type
-    uint4 pb[RT], pl[RT];
+  // One step: the softmax of step k (its scores sc were taken in the step
+  // before) and its P.V from slot cur, while the matrix cores already take
+  // step k+1's scores from slot nxt; free: the slot of step k-1, refilled
+  // with step k+3.  EDGE: some row of the wave stops inside step k
+  // (per-row masks, and a row may have seen no position yet); otherwise
+  // every score is finite.
+  // this lane's transposing reads: source lane a + 4 e of its 16-lane group
+  // addresses row e of the value group, dims 16 nb + 4 a .. +3, that is
+  // chunk 2 nb + a / 2 (stored at 2 (nb ^ e) + a / 2) and its half a % 2
+  const int tr_a = lane & 3, tr_e = (lane >> 2) & 3;
+  const int tr_lane = kq * (kWideVGroup * 16) + tr_e * 256 + (tr_a >> 1) * 16 + (tr_a & 1) * 8;
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) voff[q] = tr_lane + 32 * (q ^ tr_e);
+  f32x4_t sc[RT][2];
+  auto run_step = [&](int k, const uint4* cur, const uint4* nxt, uint4* free_slot, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const char* vcol = reinterpret_cast<const char*>(cur + kWideTok * 16);
+    // this lane's loads of step k+1 have landed (step k+2 may still be in
+    // flight) and its reads of step k-1 are done; after the barrier the same
+    // holds for every lane
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kWideBufs - 3) * kWideLoadsPerStep, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(k + kWideBufs - 1, free_slot);
+    const int tok0 = k * kWideTok;
+    // the row maxima of step k first (its scores sc were taken in the step
+    // before; masked ones become -inf), and any rescale they call for
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float x[8];
-      float mx = -INFINITY;
+      float mr = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sc[rt][h][i] * a.scale_log2;
-          if (EDGE && tok0 + 16 * h + 4 * kq + i >= lim[rt]) v = -INFINITY;
-          x[4 * h + i] = v;
-          mx = fmaxf(mx, v);
+          if (EDGE && tok0 + 16 * h + 4 * kq + i >= lim[rt]) sc[rt][h][i] = -INFINITY;
+          mr = fmaxf(mr, sc[rt][h][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));     // the row's four lanes
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mr = fmaxf(mr, __shfl_xor(mr, 16));     // the row's four lanes
+      mr = fmaxf(mr, __shfl_xor(mr, 32));
+      const float mx = (EDGE && mr == -INFINITY) ? -INFINITY : mr * c_log2;
       if (__builtin_amdgcn_ballot_w64(mx > m[rt] + kRescaleSlack) != 0) {
         const float m_new = fmaxf(m[rt], mx);
         const float f = (m_new == m[rt]) ? 1.0f : exp2_fast(m[rt] - m_new);
@@ -1459,10 +1517,21 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[rt][nb] *= f;
       }
+    }
+
+    // step k+1's scores on the matrix cores (slot nxt has landed; after the
+    // last step it holds a repeat, whose scores nobody uses), interleaved
+    // with step k's exponentials and their packing on the vector unit
+    f32x4_t sn[RT][2];
+    scores(nxt, sn);
+    uint4 pb[RT], pl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
       float pe[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pe[i] = (EDGE && x[i] == -INFINITY) ? 0.0f : exp2_fast(x[i] - m[rt]);
+        const float v = sc[rt][i >> 2][i & 3];
+        pe[i] = (EDGE && v == -INFINITY) ? 0.0f : exp2_fast(fmaf(v, c_log2, -m[rt]));
         ell[rt] += pe[i];
       }
       pb[rt].x = pack2<BF16>(pe[0], pe[1]);
@@ -1480,49 +1549,60 @@ __global__ __launch_bounds__(256) void mq_wide_kernel(const DecodeArgs a, const 
         pl[rt] = make_uint4(r[0], r[1], r[2], r[3]);
       }
     }
+    // one score product, then a share of the vector work, 16 RT times
+#pragma unroll
+    for (int i = 0; i < 8 * RT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, BF16 ? 6 : 3, 0);
+    }
 
-    // P.V: V^T operand of dims 16 nb + row, tokens 4 kq .. +3 and 16 + 4 kq .. +3
-    // (token 16 h + 4 kq + r: row r of value group 4 h + kq)
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(slot + kWideTok * 16) + kq * (kWideVGroup * 8) + row;
+    // P.V: V^T operand of dims 16 nb + row, tokens 4 kq .. +3 (value group
+    // kq) and 16 + 4 kq .. +3 (group 4 + kq), one transposing read each
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      uint32_t w[4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint16_t* g = vt + 4 * h * (kWideVGroup * 8) + 16 * nb;
-          w[2 * h + i] = (uint32_t)g[(2 * i) * 128] | ((uint32_t)g[(2 * i + 1) * 128] << 16);
-        }
-      const uint4 va = make_uint4(w[0], w[1], w[2], w[3]);
+      const char* g = vcol + (nb >> 2) * 128 + voff[nb & 3];
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)g);
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(g + 4 * kWideVGroup * 16));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo);
+      const uint2 h2 = __builtin_bit_cast(uint2, hi);
+      const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         acc[rt][nb] = mfma_k32<BF16>(va, pb[rt], acc[rt][nb]);
         if constexpr (BF16) acc[rt][nb] = mfma_k32<BF16>(va, pl[rt], acc[rt][nb]);
       }
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      sc[rt][0] = sn[rt][0];
+      sc[rt][1] = sn[rt][1];
+    }
   };
 
-  // prologue: steps 0 .. 2 in flight
+  // prologue: steps 0 .. 2 in flight, then step 0's scores
   issue(0, ring0);
   issue(1, ring1);
   issue(2, ring2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((kWideBufs - 2) * kWideLoadsPerStep, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  scores(ring0, sc);
   // steps every live row of the wave sees whole, four at a time so that each
   // slot is a fixed object; then the rest with masks
   const int k_edge = min(nsteps, wave_lim_min / kWideTok);
   int k = 0;
   for (; k + 4 <= k_edge; k += 4) {
-    run_step(k, ring0, ring3, std::false_type{});
-    run_step(k + 1, ring1, ring0, std::false_type{});
-    run_step(k + 2, ring2, ring1, std::false_type{});
-    run_step(k + 3, ring3, ring2, std::false_type{});
+    run_step(k, ring0, ring1, ring3, std::false_type{});
+    run_step(k + 1, ring1, ring2, ring0, std::false_type{});
+    run_step(k + 2, ring2, ring3, ring1, std::false_type{});
+    run_step(k + 3, ring3, ring0, ring2, std::false_type{});
   }
   for (; k < nsteps; ++k) {
     switch (k & 3) {
-      case 0: run_step(k, ring0, ring3, std::true_type{}); break;
-      case 1: run_step(k, ring1, ring0, std::true_type{}); break;
-      case 2: run_step(k, ring2, ring1, std::true_type{}); break;
-      default: run_step(k, ring3, ring2, std::true_type{}); break;
+      case 0: run_step(k, ring0, ring1, ring3, std::true_type{}); break;
+      case 1: run_step(k, ring1, ring2, ring0, std::true_type{}); break;
+      case 2: run_step(k, ring2, ring3, ring1, std::true_type{}); break;
+      default: run_step(k, ring3, ring0, ring2, std::true_type{}); break;
     }
   }
   // the clamped loads issued past the last step land before the workgroup's
