@@ -241,6 +241,21 @@ __device__ __forceinline__ void fold_partial(float& M, float& L, float (&A)[8], 
   M = Mn;
 }
 
+// the same with the partial already in registers
+__device__ __forceinline__ void fold_partial_regs(float& M, float& L, float (&A)[8], const float2 x, const float4 a0,
+                                                  const float4 a1) {
+  if (x.x == -INFINITY) return;
+  const float Mn = fmaxf(M, x.x);
+  const float fo = (M == -INFINITY) ? 0.0f : exp2_fast(M - Mn);
+  const float fn = exp2_fast(x.x - Mn);
+  L = fo * L + fn * x.y;
+  A[0] = fo * A[0] + fn * a0.x; A[1] = fo * A[1] + fn * a0.y;
+  A[2] = fo * A[2] + fn * a0.z; A[3] = fo * A[3] + fn * a0.w;
+  A[4] = fo * A[4] + fn * a1.x; A[5] = fo * A[5] + fn * a1.y;
+  A[6] = fo * A[6] + fn * a1.z; A[7] = fo * A[7] + fn * a1.w;
+  M = Mn;
+}
+
 // shared positions of group g as every pass of the grouped decode reads them
 __device__ __forceinline__ int shared_positions(const int32_t* grp_len, int ngroups, int max_shared, int g) {
   if (g < 0 || g >= ngroups) return 0;
@@ -432,6 +447,38 @@ __global__ __launch_bounds__(NW * 64) void decode_attention_kernel(const DecodeA
   const bool empty_fold = SUF && a.fold && nparts == 0 && p == 0;
   if (p >= nparts && !empty_fold) return;
   const int t_end = empty_fold ? t_begin : min(n, t_begin + plen);
+
+  // Suffix pass that stores the output itself: the first two group-pass
+  // partials of this thread's row are requested now, so that they arrive
+  // while the suffix's own positions load (folded in the same order as the
+  // rest, after the suffix)
+  constexpr int kPre = 2;
+  float2 gp_ml[kPre];
+  float4 gp_a0[kPre], gp_a1[kPre];
+  int gp_np = 0, gp_row = 0;
+  size_t gp_base = 0;
+  if constexpr (SUF) {
+    if (a.fold && threadIdx.x < G * 16 && start > 0) {
+      const int first = min(max(a.q_start[grp], 0), a.S);
+      const int w = s - first;
+      const int r = w * G + (int)(threadIdx.x >> 4);   // row among the group's rows
+      if (w >= 0 && r / 16 < a.gntiles) {
+        gp_np = (start + a.gpart_tokens - 1) / a.gpart_tokens;
+        gp_row = r % 16;
+        gp_base = (((size_t)grp * a.gntiles + r / 16) * a.Hkv + kvh) * (size_t)a.gparts_max;
+        const int wc0 = threadIdx.x & 15;
+#pragma unroll
+        for (int pp = 0; pp < kPre; ++pp) {
+          if (pp < gp_np) {
+            gp_ml[pp] = *reinterpret_cast<const float2*>(a.gws_ml + ((gp_base + pp) * 16 + gp_row) * 2);
+            const float4* ga = reinterpret_cast<const float4*>(a.gws_acc + ((gp_base + pp) * 16 + gp_row) * kD + 8 * wc0);
+            gp_a0[pp] = ga[0];
+            gp_a1[pp] = ga[1];
+          }
+        }
+      }
+    }
+  }
 
   __shared__ uint4 s_q[G * 16];
   __shared__ __attribute__((aligned(16))) float s_p[NW][2][4][4 * G];
@@ -758,7 +805,12 @@ __global__ __launch_bounds__(NW * 64) void decode_attention_kernel(const DecodeA
       // one suffix partition: add the group's shared-prefix partials (the
       // group pass finished one launch earlier) and store the result
       if (worker) {
-        fold_group_partials<G>(a, s, grp, start, kvh, wh, wc, M, Lsum, A);
+#pragma unroll
+        for (int pp = 0; pp < kPre; ++pp)
+          if (pp < gp_np) fold_partial_regs(M, Lsum, A, gp_ml[pp], gp_a0[pp], gp_a1[pp]);
+        for (int pp = kPre; pp < gp_np; ++pp)
+          fold_partial(M, Lsum, A, a.gws_ml + ((gp_base + pp) * 16 + gp_row) * 2,
+                       a.gws_acc + ((gp_base + pp) * 16 + gp_row) * kD + 8 * wc);
         const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
         float o[8];
 #pragma unroll
