@@ -798,6 +798,43 @@ def test_multi_query_wide_path_both_orders(G, Hkv, B, dtype, max_q):
     _say(f"worst max_abs {worst:.2e}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.3535534])
+def test_multi_query_wide_path_scales(dtype, scale):
+    """The wide path's scores enter the exponent as one fused multiply-add
+    with a positive factor: a negative scale flips the query's sign, a zero
+    scale gives uniform weights over the visible positions, a large one
+    sharp weights.  Each against the oracle, whose softmax takes the scale
+    as given."""
+    from oracle.decode import multi_query_one
+    from paged_kv_cache_239_amd import multi_query_workspace
+    G, Hkv, B, max_q = 4, 2, 16, 64
+    _say(f"multi-query wide scale={scale} {dtype}")
+    rng = np.random.default_rng(7100 + int(1000 * abs(scale)) + (scale < 0))
+    lens = [64, 900, 100, 333, 64 + 31]
+    nqs = [64, 64, 40, 64, 64]
+    S = len(lens)
+    Hq = G * Hkv
+    pool, host, tables, _ = _direct_case(rng, S, Hq, Hkv, B, dtype, lens)
+    T = int(sum(nqs))
+    q = round_to_dtype_bits(rng.standard_normal((T, Hq, 128)).astype(np.float32), dtype)
+    q_start = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    scale = float(np.float32(scale))
+    ws = multi_query_workspace(pool, S, Hq, max(lens), max_q)
+    out = torch.full_like(to_device_bits(q, dtype), float("nan"))
+    pool.multi_query_attention(0, out, to_device_bits(q, dtype), torch.from_numpy(q_start).cuda(),
+                               torch.from_numpy(tables).cuda(), torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(),
+                               max(lens), max_q, scale, workspace=ws,
+                               host_context_lens=np.asarray(lens, dtype=np.int32))
+    torch.cuda.synchronize()
+    got = to_host_f64(out, dtype)
+    for s in range(S):
+        rows = slice(q_start[s], q_start[s + 1])
+        ref = multi_query_one(host, 0, q[rows], tables[s], lens[s], scale, dtype)
+        ok, st = within_tolerance(got[rows], ref, dtype)
+        assert ok, (s, lens[s], nqs[s], st)
+
+
 def test_multi_query_one_query_each_matches_decode_within_tolerance():
     """nq = 1 everywhere: the multi-query path agrees with the oracle's decode
     (and so with pa_decode_attention) on the same inputs."""
