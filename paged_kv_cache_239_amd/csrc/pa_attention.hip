@@ -1000,6 +1000,11 @@ __device__ __forceinline__ f32x4_t mfma_k16(const uint2 a, const uint2 b, f32x4_
 }
 
 constexpr int kVRow = 288;   // bytes per token row of the LDS value tile (256 + 32 pad)
+
+// operand of the transposing LDS read (ds_read_b64_tr_b16)
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
 constexpr int kKRow = 272;   // bytes per token row of an LDS key tile (256 + 16 pad)
 
 
@@ -1132,6 +1137,8 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
     }
   };
 
+  // this lane's transposing value read: token 4 kq + (lane / 4) % 4, dims 4 (lane % 4) ..
+  const int tr_lane = (4 * kq + ((lane >> 2) & 3)) * kVRow + (lane & 3) * 8;
   int buf = 0;
   auto process_group = [&](int g, const uint4 (&K)[4], const uint4 (&V)[4], bool tail) {
     const int tok0 = g * 16;
@@ -1140,9 +1147,9 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
     buf ^= 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // token t = 4j + kq: key row t, value row (t % 4) * 4 + t / 4 = kq * 4 + j
+      // token t = 4j + kq: key row t, value row t
       *reinterpret_cast<uint4*>(kb + (4 * j + kq) * kKRow + row * 16) = K[j];
-      *reinterpret_cast<uint4*>(vb + (kq * 4 + j) * kVRow + row * 16) = V[j];
+      *reinterpret_cast<uint4*>(vb + (4 * j + kq) * kVRow + row * 16) = V[j];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1192,14 +1199,14 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(vb);
+    // V^T operand of dims 16 nb + row, tokens 4 kq .. +3: one transposing
+    // read (lane a + 4 e of the 16-lane group kq addresses token 4 kq + e,
+    // dims 16 nb + 4 a .. +3; lane 4 a + b receives dim 16 nb + 4 a + b of the
+    // four tokens); the 32-byte row padding spreads each half-wave over all banks
+    const char* vtr = vb + tr_lane;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      // V[token 4kq + i][dim 16nb + row] sits at LDS row i * 4 + kq
-      const int col = 16 * nb + row;
-      uint2 va;
-      va.x = (uint32_t)vt[((0 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((1 * 4 + kq) * kVRow) / 2 + col] << 16);
-      va.y = (uint32_t)vt[((2 * 4 + kq) * kVRow) / 2 + col] | ((uint32_t)vt[((3 * 4 + kq) * kVRow) / 2 + col] << 16);
+      const uint2 va = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vtr + 32 * nb)));
       acc[nb] = mfma_k16<BF16>(va, pb, acc[nb]);
       if constexpr (BF16) acc[nb] = mfma_k16<BF16>(va, pl, acc[nb]);
     }
@@ -1327,8 +1334,6 @@ constexpr int kWideSlot = kWideTok * 16 + (kWideTok / 4) * kWideVGroup;   // chu
 constexpr int kWideLoadsPerStep = 4;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // s_waitcnt immediate (gfx9 layout): vector-memory count vm, LDS count lgkm,
 // export count left at its maximum
