@@ -1301,9 +1301,10 @@ __global__ __launch_bounds__(NW * 64) void mq_mfma_kernel(const DecodeArgs a, co
 // whose reads of the context mostly hit its L2.  Four waves own RT 16-row
 // tiles each (wave w: rows 16 RT w ..); all waves share the 32-token steps.
 // Keys and values travel from HBM straight into a ring of four LDS slots
-// (direct-to-LDS loads, no registers in between), so three steps are in
-// flight while one is computed; one barrier per step both publishes the
-// step that landed and frees the slot the step before used.  A load
+// (direct-to-LDS loads, no registers in between): while step k's softmax
+// and P.V run and step k+1's scores are taken, steps k+2 and k+3 are in
+// flight; one barrier per step both publishes the step that landed and
+// frees the slot the step before used.  A load
 // instruction fills 1 KB of LDS (four token rows), lane by lane.  Key rows:
 // token t's 16-byte chunk c sits at position c ^ (t % 16), so the 16 tokens
 // whose rows one MFMA operand reads spread over all banks.  Values: each
