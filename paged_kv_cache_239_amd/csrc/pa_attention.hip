@@ -965,11 +965,10 @@ __global__ __launch_bounds__(G * 16) void cascade_merge_kernel(const DecodeArgs 
 //       tokens 4kq .. 4kq+3 for its row;
 //   O^T[dim][row] += V^T[dim][token] . P^T[token][row]   8 x mfma 16x16x16:
 //       B = the lane's own four probabilities (the layout S^T came out in),
-//       A = V^T, read from a per-wave LDS copy of the value tile (token t
-//       stored at row (t % 4) * 4 + t / 4, 288-byte stride: the four quarters
-//       of a wave hit disjoint banks); lane (row, kq) accumulates dims
-//       16nb + 4kq .. +3 of its row, so the softmax state of a row and its
-//       rescale stay inside the lane.
+//       A = V^T, from a per-wave LDS copy of the value tile (token order,
+//       288-byte rows) by one transposing read (ds_read_b64_tr_b16) per 16
+//       dims; lane (row, kq) accumulates dims 16nb + 4kq .. +3 of its row, so
+//       the softmax state of a row and its rescale stay inside the lane.
 // Probabilities enter the P.V products in the storage type (the products
 // accumulate in fp32); for bf16 as a rounded part plus the rounded remainder.
 // ---------------------------------------------------------------------------
