@@ -835,6 +835,45 @@ def test_multi_query_wide_path_scales(dtype, scale):
         assert ok, (s, lens[s], nqs[s], st)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_multi_query_wide_path_table_beyond_lds(dtype):
+    """A context whose table row exceeds the 2,048 entries the wide kernel
+    caches in LDS (B = 8, 17,000 and 16,400 positions): its blocks are read
+    from the table in memory instead.  Against the oracle, both launch
+    orders, beside a short sequence that takes the cached path."""
+    from oracle.decode import multi_query_one
+    from paged_kv_cache_239_amd import multi_query_workspace
+    G, Hkv, B, max_q = 4, 1, 8, 40
+    _say(f"multi-query wide, long table, {dtype}")
+    rng = np.random.default_rng(7300 + (dtype == "f16"))
+    lens = [17000, 300, 16400]
+    nqs = [40, 40, 33]
+    S = len(lens)
+    Hq = G * Hkv
+    pool, host, tables, _ = _direct_case(rng, S, Hq, Hkv, B, dtype, lens)
+    T = int(sum(nqs))
+    q = round_to_dtype_bits(rng.standard_normal((T, Hq, 128)).astype(np.float32), dtype)
+    q_start = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    ws = multi_query_workspace(pool, S, Hq, max(lens), max_q)
+    dq = to_device_bits(q, dtype)
+    outs = []
+    for ordered in (False, True):
+        out = torch.full_like(dq, float("nan"))
+        pool.multi_query_attention(0, out, dq, torch.from_numpy(q_start).cuda(), torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(), max(lens), max_q, scale,
+                                   workspace=ws, host_context_lens=np.asarray(lens, dtype=np.int32) if ordered else None)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    got = to_host_f64(outs[1], dtype)
+    for s in range(S):
+        rows = slice(q_start[s], q_start[s + 1])
+        ref = multi_query_one(host, 0, q[rows], tables[s], lens[s], scale, dtype)
+        ok, st = within_tolerance(got[rows], ref, dtype)
+        assert ok, (s, lens[s], nqs[s], st)
+
+
 def test_multi_query_one_query_each_matches_decode_within_tolerance():
     """nq = 1 everywhere: the multi-query path agrees with the oracle's decode
     (and so with pa_decode_attention) on the same inputs."""
