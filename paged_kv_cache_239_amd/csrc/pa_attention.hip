@@ -687,8 +687,10 @@ __global__ __launch_bounds__(NW * 64) void decode_attention_kernel(const DecodeA
     const int ng = g_full > g_first ? (g_full - g_first + NW - 1) / NW : 0;
     uint4 K0[4], V0[4], K1[4], V1[4];
     // unconditional, so that every path has the same loads in flight (a wave
-    // without a full group reads an in-bounds stand-in block and ignores it)
-    load_group(0, K0, V0, false);
+    // without a full group reads an in-bounds stand-in block and ignores it);
+    // in the suffix pass, whose suffixes are mostly shorter than one group,
+    // only when there is a full group, so the tail is not read twice
+    if (!SUF || ng > 0) load_group(0, K0, V0, false);
     if (threadIdx.x < G * 16) s_q[threadIdx.x] = qv;
     __syncthreads();
 #pragma unroll
